@@ -1,0 +1,308 @@
+/*
+ * CPU oracle for the HSTU block forward with a paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; both follow the same written
+ * definition independently.
+ *
+ * What it computes (all arithmetic in double; inputs are float values, which
+ * in bf16 workloads are exactly representable in bf16):
+ *
+ *   HSTU block ("How Generative Recommenders Are Redefining RecSys at Scale",
+ *   section HSTU: softmax replaced by SiLU-based weighting, a relative
+ *   attention bias, elementwise gating before the output projection), with
+ *   the equations
+ *       x^   = LayerNorm(x)                       (over d, biased variance, no affine)
+ *       [U|V|Q|K] = SiLU(x^ . W1)                 (column chunks, head-major inside)
+ *       o_i  = (1/n) sum_{j in M(i)} SiLU(q_i.k_j + rab[b(i-j)]) v_j    (per head)
+ *       g    = LayerNorm(o) (*) U                 (over all heads concatenated)
+ *       y    = x + g . W2
+ *   M(i) = {j <= i} for history queries, {j < history length} u {i} for
+ *   candidate queries; b(delta) = min(nb-1, floor(4 log2(1+delta))).
+ *
+ *   KV cache ("Deploying an HSTU Generative Recommender with NVIDIA
+ *   Dynamo-Triton": a paged KV data table with lookup, allocation, append and
+ *   eviction, LRU-style eviction of older users when space is tight; the
+ *   attention reads the cache directly): an allocator with a FIFO free-page
+ *   queue, whole-user LRU eviction, and a canonical state dump.
+ *
+ * Sums run in ascending index order.  OpenMP splits only independent outputs
+ * (rows, (user, head, query) triples); it does not change any summation.
+ * Build: gcc -O2 -fopenmp -fPIC -shared (no -ffast-math).
+ *
+ * Compile-time ORACLE_MUTANT=k plants one deliberate mistake (used only by
+ * the tests that prove the pins catch such mistakes).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define OK 0
+#define ERR_INVALID 1
+#define ERR_NO_SPACE 2
+#define ERR_UNKNOWN_USER 3
+
+/* ------------------------------------------------------------------------ */
+/* elementwise pieces                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) */
+double oracle_silu(double z) {
+#if ORACLE_MUTANT == 1
+  return z / (1.0 + exp(z)); /* planted: wrong sign in the exponent */
+#else
+  return z / (1.0 + exp(-z));
+#endif
+}
+
+/* LayerNorm without affine: (x - mean) / sqrt(var + eps), biased variance. */
+void oracle_layer_norm(const double *x, int n, double eps, double *out) {
+  double mean = 0.0;
+  for (int k = 0; k < n; ++k) mean += x[k];
+  mean /= n;
+  double var = 0.0;
+  for (int k = 0; k < n; ++k) var += (x[k] - mean) * (x[k] - mean);
+  var /= n;
+#if ORACLE_MUTANT == 2
+  double inv = 1.0 / sqrt(var); /* planted: eps dropped */
+#else
+  double inv = 1.0 / sqrt(var + eps);
+#endif
+  for (int k = 0; k < n; ++k) out[k] = (x[k] - mean) * inv;
+}
+
+/* Relative-position bucket b(delta) = min(nb - 1, floor(4 * log2(1 + delta))),
+ * evaluated exactly: floor(4 log2 m) = floor(log2(m^4)) = bit length of m^4
+ * minus one, with m = 1 + delta. */
+int oracle_bucket(int64_t delta, int num_buckets) {
+  if (delta < 0) return -1;
+  unsigned __int128 m = (unsigned __int128)(delta + 1);
+  unsigned __int128 p = m * m * m * m;
+  int b = 0;
+  while ((p >> (b + 1)) != 0) ++b;
+#if ORACLE_MUTANT == 3
+  b = b / 2; /* planted: wrong bucket scale */
+#endif
+  return b < num_buckets - 1 ? b : num_buckets - 1;
+}
+
+/* Visibility of key position j to query position i for a user whose first
+ * `hist` positions are history and the rest candidates. */
+static int visible(int64_t i, int64_t j, int64_t hist) {
+#if ORACLE_MUTANT == 4
+  return j <= i; /* planted: candidates see each other (plain causal) */
+#else
+  if (j == i) return 1;
+  return j < i && j < hist;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* attention over a jagged batch                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * q      [N_new][H][dh]   queries of the new tokens (user u's new tokens are
+ *                          rows q_off[u] .. q_off[u+1]-1, at positions
+ *                          start[u] .. start[u] + t_u - 1)
+ * k, v   [sum L_u][H][dh] every key/value of user u (positions 0..L_u-1) at
+ *                          rows kv_off[u] .. kv_off[u+1]-1
+ * n_targets[u]             T_u: the last T_u positions are candidates
+ * norm_n[u]                n_u
+ * rab[num_buckets]         bias table of the layer (shared by the heads)
+ * o      [N_new][H][dh]   output (A V), already divided by n_u
+ */
+int oracle_attention(int B, int H, int dh, const int64_t *q_off, const int64_t *start,
+                     const int64_t *kv_off, const int64_t *n_targets, const double *norm_n,
+                     const double *q, const double *k, const double *v, const double *rab,
+                     int num_buckets, double *o) {
+  if (B < 0 || H <= 0 || dh <= 0 || num_buckets <= 0) return ERR_INVALID;
+  for (int u = 0; u < B; ++u) {
+    int64_t t_u = q_off[u + 1] - q_off[u];
+    int64_t L_u = kv_off[u + 1] - kv_off[u];
+    if (t_u < 0 || L_u < 0 || start[u] < 0 || start[u] + t_u > L_u) return ERR_INVALID;
+    if (n_targets[u] < 0 || n_targets[u] > L_u) return ERR_INVALID;
+  }
+  int64_t n_new = q_off[B];
+  int64_t total = n_new * H;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t task = 0; task < total; ++task) {
+    int64_t row = task / H;
+    int h = (int)(task % H);
+    int u = 0;
+    while (q_off[u + 1] <= row) ++u;
+    int64_t L_u = kv_off[u + 1] - kv_off[u];
+    int64_t hist = L_u - n_targets[u];
+    int64_t i = start[u] + (row - q_off[u]);
+    const double *qi = q + (row * H + h) * dh;
+    double *oi = o + (row * H + h) * dh;
+    for (int e = 0; e < dh; ++e) oi[e] = 0.0;
+    for (int64_t j = 0; j < L_u; ++j) {
+      if (!visible(i, j, hist)) continue;
+      const double *kj = k + ((kv_off[u] + j) * H + h) * dh;
+      const double *vj = v + ((kv_off[u] + j) * H + h) * dh;
+      double s = 0.0;
+      for (int e = 0; e < dh; ++e) s += qi[e] * kj[e];
+#if ORACLE_MUTANT == 5
+      /* planted: bias dropped */
+#elif ORACLE_MUTANT == 6
+      s += rab[oracle_bucket(i - j + 1, num_buckets)]; /* planted: off-by-one distance */
+#else
+      s += rab[oracle_bucket(i - j, num_buckets)];
+#endif
+      double w = oracle_silu(s);
+      for (int e = 0; e < dh; ++e) oi[e] += w * vj[e];
+    }
+#if ORACLE_MUTANT == 7
+    double n = norm_n[u] + 1.0; /* planted: wrong normalizer */
+#else
+    double n = norm_n[u];
+#endif
+    for (int e = 0; e < dh; ++e) oi[e] /= n;
+  }
+  return OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* one HSTU layer                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * x        [N_new][d] double  layer input of the new tokens (jagged by q_off)
+ * w1       [d][4*H*dh] float  f1, used as x^ . W1; column chunks U, V, Q, K
+ * w2       [H*dh][d] float    f2
+ * rab      [num_buckets] float
+ * start[u]                    c_u: cached positions of user u (new tokens follow)
+ * hist_k/v [sum c_u][H][dh] double  cached K/V of each user, rows hist_off[u]..
+ * Outputs (double; any may be NULL except y):
+ *   xhat [N_new][d], u/v/q/k [N_new][H*dh], o [N_new][H*dh], g [N_new][H*dh], y [N_new][d]
+ */
+int oracle_layer(int B, int d, int H, int dh, double eps, const int64_t *q_off,
+                 const int64_t *start, const int64_t *n_targets, const double *norm_n,
+                 const double *x, const float *w1, const float *w2, const float *rab,
+                 int num_buckets, const int64_t *hist_off, const double *hist_k,
+                 const double *hist_v, double *xhat_out, double *u_out, double *v_out,
+                 double *q_out, double *k_out, double *o_out, double *g_out, double *y) {
+  if (B < 0 || d <= 0 || H <= 0 || dh <= 0 || !y) return ERR_INVALID;
+  for (int u = 0; u < B; ++u)
+    if (hist_off[u + 1] - hist_off[u] != start[u]) return ERR_INVALID;
+  const int inner = H * dh;
+  const int64_t n_new = q_off[B];
+  double *xh = (double *)malloc(sizeof(double) * (size_t)(n_new * d + 1));
+  double *s = (double *)malloc(sizeof(double) * (size_t)(n_new * 4 * inner + 1));
+  double *o = (double *)malloc(sizeof(double) * (size_t)(n_new * inner + 1));
+  double *g = (double *)malloc(sizeof(double) * (size_t)(n_new * inner + 1));
+  int64_t *kv_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B + 1));
+  if (!xh || !s || !o || !g || !kv_off) return ERR_INVALID;
+
+  /* 1. pre-norm */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_new; ++r) {
+    double tmp[d];
+    for (int c = 0; c < d; ++c) tmp[c] = x[r * d + c];
+    oracle_layer_norm(tmp, d, eps, xh + r * d);
+  }
+  /* 2. f1 then SiLU */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_new; ++r) {
+    for (int c = 0; c < 4 * inner; ++c) {
+      double z = 0.0;
+      for (int kk = 0; kk < d; ++kk) {
+#if ORACLE_MUTANT == 8
+        z += xh[r * d + kk] * (double)w1[(int64_t)c * d + kk]; /* planted: W1 read transposed */
+#else
+        z += xh[r * d + kk] * (double)w1[(int64_t)kk * 4 * inner + c];
+#endif
+      }
+      s[r * 4 * inner + c] = oracle_silu(z);
+    }
+  }
+  /* 3. split [U|V|Q|K]; 4. full K/V sequence of each user = cached + new */
+  kv_off[0] = 0;
+  for (int u = 0; u < B; ++u) kv_off[u + 1] = kv_off[u] + start[u] + (q_off[u + 1] - q_off[u]);
+  double *kf = (double *)malloc(sizeof(double) * (size_t)(kv_off[B] * inner + 1));
+  double *vf = (double *)malloc(sizeof(double) * (size_t)(kv_off[B] * inner + 1));
+  double *qn = (double *)malloc(sizeof(double) * (size_t)(n_new * inner + 1));
+  if (!kf || !vf || !qn) return ERR_INVALID;
+  for (int u = 0; u < B; ++u) {
+    for (int64_t j = 0; j < start[u]; ++j)
+      for (int c = 0; c < inner; ++c) {
+        kf[(kv_off[u] + j) * inner + c] = hist_k[(hist_off[u] + j) * inner + c];
+        vf[(kv_off[u] + j) * inner + c] = hist_v[(hist_off[u] + j) * inner + c];
+      }
+    for (int64_t r = q_off[u]; r < q_off[u + 1]; ++r) {
+      int64_t j = start[u] + (r - q_off[u]);
+      const double *sr = s + r * 4 * inner;
+      for (int c = 0; c < inner; ++c) {
+#if ORACLE_MUTANT == 9
+        /* planted: Q and K chunks swapped */
+        qn[r * inner + c] = sr[3 * inner + c];
+        kf[(kv_off[u] + j) * inner + c] = sr[2 * inner + c];
+#else
+        qn[r * inner + c] = sr[2 * inner + c];
+        kf[(kv_off[u] + j) * inner + c] = sr[3 * inner + c];
+#endif
+        vf[(kv_off[u] + j) * inner + c] = sr[1 * inner + c];
+      }
+    }
+  }
+  /* 5. attention */
+  {
+    double *rabd = (double *)malloc(sizeof(double) * (size_t)num_buckets);
+    if (!rabd) return ERR_INVALID;
+    for (int b = 0; b < num_buckets; ++b) rabd[b] = (double)rab[b];
+    int rc = oracle_attention(B, H, dh, q_off, start, kv_off, n_targets, norm_n, qn, kf, vf,
+                              rabd, num_buckets, o);
+    free(rabd);
+    if (rc != OK) return rc;
+  }
+  /* 6. LayerNorm over the concatenated heads, gate by U */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_new; ++r) {
+    double ln[inner];
+    oracle_layer_norm(o + r * inner, inner, eps, ln);
+    for (int c = 0; c < inner; ++c) {
+#if ORACLE_MUTANT == 10
+      g[r * inner + c] = ln[c] * s[r * 4 * inner + 1 * inner + c]; /* planted: gate by V */
+#else
+      g[r * inner + c] = ln[c] * s[r * 4 * inner + 0 * inner + c];
+#endif
+    }
+  }
+  /* 7. f2 plus residual */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_new; ++r) {
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int kk = 0; kk < inner; ++kk) acc += g[r * inner + kk] * (double)w2[(int64_t)kk * d + c];
+#if ORACLE_MUTANT == 11
+      y[r * d + c] = acc; /* planted: residual dropped */
+#else
+      y[r * d + c] = x[r * d + c] + acc;
+#endif
+    }
+  }
+  for (int64_t r = 0; r < n_new; ++r) {
+    int u = 0;
+    while (q_off[u + 1] <= r) ++u;
+    int64_t j = start[u] + (r - q_off[u]);
+    for (int c = 0; c < inner; ++c) {
+      if (u_out) u_out[r * inner + c] = s[r * 4 * inner + c];
+      if (v_out) v_out[r * inner + c] = vf[(kv_off[u] + j) * inner + c];
+      if (q_out) q_out[r * inner + c] = qn[r * inner + c];
+      if (k_out) k_out[r * inner + c] = kf[(kv_off[u] + j) * inner + c];
+      if (o_out) o_out[r * inner + c] = o[r * inner + c];
+      if (g_out) g_out[r * inner + c] = g[r * inner + c];
+    }
+    if (xhat_out)
+      for (int c = 0; c < d; ++c) xhat_out[r * d + c] = xh[r * d + c];
+  }
+  free(xh); free(s); free(o); free(g); free(kv_off); free(kf); free(vf); free(qn);
+  return OK;
+}
