@@ -1,0 +1,214 @@
+"""Benchmark of the HSTU block forward with a paged KV cache on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4]
+
+One step is one whole request through the hot path: restore the cache
+metadata to its pre-request state, look the batch up, evict least-recently
+used users if pages are short, allocate pages, upload the page table and the
+request plan, then run every layer (pre-norm, f1 + SiLU, K/V append,
+attention over cached + new keys, LayerNorm(AV) * U, f2 + residual) on the
+new tokens.  The new-token inputs are already in device memory when timing
+starts.  Prints one JSON line: new tokens per second, the dominant kernel
+against its roofline (duration from HIP events on its launch stream), and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+
+WORKLOAD_TEXT = {
+    "C2": "3-layer bf16 HSTU stack, full recompute (no cache): batch 8, d_model 512, 4 heads x 128, "
+          "history uniform [1024, 4096] + 64 target-aware candidates per user",
+    "C3": "3-layer bf16 HSTU stack, 100% paged-cache hit (32-token pages, permuted placement): batch 8, "
+          "d_model 512, 4 heads x 128, cached history uniform [1024, 4096], 64 new candidates per user",
+    "C4": "8-layer bf16 HSTU stack, batch 8, d_model 512, 4 heads x 128; history lognormal(median 2048, "
+          "sigma 1) clipped to [256, 8192] + 64 candidates; 50% of users hit a paged cache (32-token "
+          "pages), the rest prefill and append; the pool forces LRU eviction of stale users",
+    "C5": "8-layer bf16 HSTU stack, batch 128, d_model 512, 4 heads x 128; history lognormal(median 2048, "
+          "sigma 1) clipped to [128, 16384], 100% paged-cache hit (64-token pages), 256 target-aware "
+          "candidates, 128 rab buckets",
+}
+
+
+def attention_bytes(req, H, dh, es=2):
+    """Algorithmic HBM bytes of one attention launch: every visible key/value
+    row once per (user, head), the queries once, the fp32 output once."""
+    kv = 0
+    for c, t, T in zip(req.cached_len, req.new_len, req.n_targets):
+        if t == 0:
+            continue
+        kv += int(c + t)
+    n = int(sum(req.new_len))
+    return kv * H * dh * 2 * es + n * H * dh * (es + 4)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4", choices=["C2", "C3", "C4", "C5"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from generative_recommender_sequence_amd import hstu, runtime
+    from generative_recommender_sequence_amd.workloads import workload_for
+
+    runtime.require_gpu()
+    torch.cuda.set_device(0)
+    w = workload_for(args.workload, args.seed)
+    cfg = w.cfg
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    users, new_len, n_targets, norm_n, rows = scn.request_inputs()
+    x = scn._x(rows)                       # new-token inputs resident in HBM
+    n_new = int(sum(new_len))
+
+    # size the workspace once for the request shape
+    scn.restore()
+    req0 = scn.make_request(rows)[0]
+    ws = runtime.workspace_for(scn.model, req0)
+    info0 = req0.info
+    req0.close()
+
+    def step():
+        scn.restore()
+        req = runtime.prepare(scn.cache, users, new_len, n_targets, norm_n, scn.max_pages, cfg.num_heads,
+                              cfg.head_dim)
+        y = runtime.forward(scn.model, req, x, scn.cache, ws)
+        return req, y
+
+    pending = []
+    for _ in range(args.warmup):
+        pending.append(step()[0])
+    torch.cuda.synchronize()
+    for r in pending:
+        r.close()
+    pending.clear()
+
+    hstu.hstu_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pending.append(step()[0])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = {}
+    for name in hstu.TIMED_KERNELS:
+        n, ms = hstu.hstu_timing_read(name)
+        if n:
+            kern[name] = {"launches": n, "avg_us": round(1000.0 * ms / n, 2), "ms_per_step": round(ms / args.steps, 4)}
+    hstu.hstu_timing_enable(False)
+    req_last = pending[-1]
+    for r in pending[:-1]:
+        r.close()
+    ms_per_step = 1000.0 * (t1 - t0) / args.steps
+
+    # dominant kernel: attention
+    H, dh = cfg.num_heads, cfg.head_dim
+    flops = 4.0 * dh * H * float(req_last.info.pairs)
+    bytes_ = float(attention_bytes(req_last, H, dh))
+    att_us = kern["attention"]["avg_us"]
+    cached_frac = float(sum(c for c in req_last.cached_len)) / max(1.0, float(sum(req_last.kv_len)))
+    if args.workload in ("C3", "C5"):
+        achieved = bytes_ / (att_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (att_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "attention (attn_bf16_kernel, paged)", "avg_us": att_us,
+                 "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
+                 "unmasked_pairs_per_head": int(req_last.info.pairs)})
+    req_last.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, scn, users, new_len, n_targets, norm_n, rows)
+
+    out = {
+        "metric": "HSTU new tokens/s at batch 8, 8 layers, cache hit; % HBM / MFMA roofline",
+        "value": round(n_new / (ms_per_step / 1000.0), 1),
+        "unit": "new tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal weights/inputs, random-init; shapes of the pages' benchmark)",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "global_batch": cfg.batch,
+                   "layers": cfg.num_layers, "d_model": cfg.d_model, "heads": H, "head_dim": dh,
+                   "new_tokens_per_step": n_new,
+                   "candidate_tokens_per_step": int(sum(n_targets)),
+                   "cached_key_fraction": round(cached_frac, 4),
+                   "evicted_users_per_step": int(len(scn_evicted(scn, users, new_len))),
+                   "attention_work_items": int(info0.n_work_items), "seed": args.seed},
+        "roofline": roof,
+        "kernels": kern,
+        "candidate_tokens_per_s": round(sum(n_targets) / (ms_per_step / 1000.0), 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def scn_evicted(scn, users, new_len):
+    from generative_recommender_sequence_amd import hstu
+    if scn.cache is None:
+        return []
+    scn.restore()
+    cached = hstu.kv_lookup(scn.cache.h, users)
+    need = scn.cache.pages_needed(cached, new_len)
+    ev = hstu.kv_evict_lru(scn.cache.h, need, users) if hstu.kv_free_pages(scn.cache.h) < need else []
+    scn.restore()
+    return ev
+
+
+def cpu_baseline(w, scn, users, new_len, n_targets, norm_n, rows):
+    """The oracle on layer 0 of the same request (every user; hit users attend
+    to a seeded random history of their cached length), scaled to the stack's
+    layer count."""
+    import oracle
+
+    cfg = w.cfg
+    inner = cfg.inner
+    cached = [int(w.hist_len[b]) if w.hit[b] else 0 for b in range(cfg.batch)]
+    rng = np.random.default_rng(1234)
+    hk = rng.standard_normal((sum(cached), inner)) * 0.1
+    hv = rng.standard_normal((sum(cached), inner)) * 0.1
+    x = np.concatenate(rows).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.layer(x, w.layers[0].w1, w.layers[0].w2, w.layers[0].rab, new_len, cached, n_targets, norm_n, hk, hv,
+                 cfg.num_heads, cfg.head_dim, cfg.eps)
+    dt = time.perf_counter() - t0
+    per_step = dt * cfg.num_layers
+    return {"value": round(sum(new_len) / per_step, 2), "unit": "new tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 of one {cfg.name} request ({sum(new_len)} new tokens, all {cfg.batch} users), "
+                      f"{dt:.1f} s, scaled by {cfg.num_layers} layers"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,502 @@
+// C ABI of libhstu: error state, the request plan (a host-side schedule of
+// the attention work, built once per request and reused by every layer),
+// and the drivers of hstu_attn_fwd / hstu_layer_forward / kv_page_append /
+// kv_page_gather.  Every arithmetic step runs in the HIP kernels under
+// kernels/; this file only validates, schedules and launches.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+
+#include "internal.h"
+
+namespace hstu {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+hstu_status fail(hstu_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+hstu_status ok() {
+  g_last_error.clear();
+  return HSTU_OK;
+}
+hstu_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HSTU_OK;
+  return fail(HSTU_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+namespace {
+
+template <typename F>
+hipError_t timed(TimedKernel k, hipStream_t s, F&& f) {
+  TimedLaunch t(k, s);
+  hipError_t e = f();
+  t.end();
+  return e;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
+
+// Attention work per key tile is roughly constant, so pieces are sized in
+// visible tiles.  Enough pieces to give every CU several, but never pieces so
+// small that their partial tile costs more than the keys they read.
+constexpr int kTargetPieces = 1024;
+constexpr int kMinPieceTiles = 4;
+
+bool tile_visible(int64_t k0, int64_t qa, int64_t qe, int64_t hist) {
+  // some key j in [k0, k0+kTileK) visible to some query i in [qa, qe):
+  // either j == i for some i, or j < i and j < hist
+  int64_t k1 = k0 + kTileK;
+  if (k0 < qe && qa < k1) return true;
+  return k0 < hist && k0 < qe - 1;
+}
+
+}  // namespace
+}  // namespace hstu
+
+using namespace hstu;
+
+extern "C" {
+
+const char* hstu_last_error(void) { return g_last_error.c_str(); }
+int32_t hstu_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
+  if (!d || !out) return fail(HSTU_ERR_INVALID, "hstu_plan_create: null argument");
+  *out = nullptr;
+  const int32_t B = d->B, H = d->num_heads, dh = d->head_dim;
+  if (B < 0 || H <= 0 || dh <= 0) return fail(HSTU_ERR_INVALID, "hstu_plan_create: bad B/H/dh");
+  if (B > 0 && (!d->new_len || !d->cached_len || !d->n_targets))
+    return fail(HSTU_ERR_INVALID, "hstu_plan_create: null per-user array");
+  if (dh != 32 && dh != 64 && dh != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "hstu_plan_create: head_dim must be 32, 64 or 128");
+  if (d->page_size < 0 || (d->page_size > 0 && d->max_pages <= 0))
+    return fail(HSTU_ERR_INVALID, "hstu_plan_create: bad page_size/max_pages");
+  auto* p = new hstu_plan();
+  p->desc = *d;
+  p->new_len.assign(d->new_len, d->new_len + B);
+  p->cached_len.assign(d->cached_len, d->cached_len + B);
+  p->n_targets.assign(d->n_targets, d->n_targets + B);
+  p->norm_n.resize(B);
+  p->desc.new_len = p->desc.cached_len = p->desc.n_targets = nullptr;
+  p->desc.norm_n = nullptr;
+  int64_t q_row = 0, kv_row = 0;
+  p->new_offsets.push_back(0);
+  for (int32_t u = 0; u < B; ++u) {
+    int64_t t = p->new_len[u], c = p->cached_len[u], T = p->n_targets[u];
+    int64_t L = t + c;
+    if (t < 0 || c < 0 || T < 0 || T > L) {
+      delete p;
+      return fail(HSTU_ERR_INVALID, "hstu_plan_create: bad new_len/cached_len/n_targets");
+    }
+    if (L > kMaxPos) {
+      delete p;
+      return fail(HSTU_ERR_UNSUPPORTED, "hstu_plan_create: sequence longer than 65535");
+    }
+    if (d->page_size > 0 && L > static_cast<int64_t>(d->max_pages) * d->page_size) {
+      delete p;
+      return fail(HSTU_ERR_INVALID, "hstu_plan_create: max_pages * page_size < sequence length");
+    }
+    float n = d->norm_n ? d->norm_n[u] : static_cast<float>(L);
+    if (t > 0 && (!(n > 0.f) || !std::isfinite(n))) {
+      delete p;
+      return fail(HSTU_ERR_INVALID, "hstu_plan_create: norm_n must be positive");
+    }
+    p->norm_n[u] = n;
+    UserInfo ui{};
+    ui.q_row0 = static_cast<int32_t>(q_row);
+    ui.n_new = static_cast<int32_t>(t);
+    ui.start = static_cast<int32_t>(c);
+    ui.kv_len = static_cast<int32_t>(L);
+    ui.hist = static_cast<int32_t>(L - T);
+    ui.kv_row0 = static_cast<int32_t>(kv_row);
+    ui.inv_n = t > 0 ? 1.0f / n : 0.0f;
+    p->users.push_back(ui);
+    p->start_pos.push_back(static_cast<int32_t>(c));
+    q_row += t;
+    kv_row += L;
+    if (q_row > INT32_MAX / 4 || kv_row > INT32_MAX / 4) {
+      delete p;
+      return fail(HSTU_ERR_UNSUPPORTED, "hstu_plan_create: batch too large");
+    }
+    p->new_offsets.push_back(static_cast<int32_t>(q_row));
+    p->max_len = std::max<int32_t>(p->max_len, static_cast<int32_t>(L));
+    // unmasked pairs of this user's new queries
+    for (int64_t i = c; i < L; ++i) p->pairs += (i < L - T) ? (i + 1) : (L - T + 1);
+  }
+  p->n_new = static_cast<int32_t>(q_row);
+
+  // q-blocks
+  p->row_qblock.resize(p->n_new);
+  for (int32_t u = 0; u < B; ++u) {
+    const UserInfo& ui = p->users[u];
+    for (int32_t r = 0; r < ui.n_new; r += kBlockQ) {
+      QBlock qb{u, ui.q_row0 + r, std::min(kBlockQ, ui.n_new - r), ui.start + r};
+      for (int32_t k = 0; k < qb.count; ++k)
+        p->row_qblock[qb.row0 + k] = static_cast<int32_t>(p->qblocks.size());
+      p->qblocks.push_back(qb);
+    }
+  }
+  // visible key tiles of each q-block, then pieces
+  const int32_t nqb = static_cast<int32_t>(p->qblocks.size());
+  std::vector<std::vector<int32_t>> vis(nqb);
+  int64_t total = 0;
+  for (int32_t b = 0; b < nqb; ++b) {
+    const QBlock& qb = p->qblocks[b];
+    const UserInfo& ui = p->users[qb.user];
+    int64_t qa = qb.pos0, qe = qb.pos0 + qb.count;
+    int32_t ntiles = static_cast<int32_t>((qe + kTileK - 1) / kTileK);
+    for (int32_t t = 0; t < ntiles; ++t)
+      if (tile_visible(static_cast<int64_t>(t) * kTileK, qa, qe, ui.hist)) vis[b].push_back(t);
+    total += static_cast<int64_t>(vis[b].size()) * H;
+  }
+  int64_t piece_tiles =
+      std::max<int64_t>(kMinPieceTiles, (total + kTargetPieces - 1) / kTargetPieces);
+  p->qb_slots.resize(static_cast<size_t>(nqb) * H);
+  std::vector<std::pair<int32_t, WorkItem>> pieces;  // (visible tiles, item)
+  int32_t slot = 0;
+  for (int32_t b = 0; b < nqb; ++b) {
+    const auto& v = vis[b];
+    int32_t nv = static_cast<int32_t>(v.size());
+    int32_t np = std::max<int32_t>(1, static_cast<int32_t>((nv + piece_tiles - 1) / piece_tiles));
+    for (int32_t h = 0; h < H; ++h) {
+      p->qb_slots[static_cast<size_t>(b) * H + h] = SlotRange{slot, np};
+      for (int32_t k = 0; k < np; ++k) {
+        int32_t lo = static_cast<int32_t>(static_cast<int64_t>(nv) * k / np);
+        int32_t hi = static_cast<int32_t>(static_cast<int64_t>(nv) * (k + 1) / np);
+        WorkItem w{};
+        w.user = p->qblocks[b].user;
+        w.head = h;
+        w.qblock = b;
+        w.tile_begin = nv ? v[lo] : 0;
+        w.tile_end = nv ? v[hi - 1] + 1 : 0;
+        w.slot = slot++;
+        pieces.emplace_back(hi - lo, w);
+      }
+    }
+  }
+  p->n_slots = slot;
+  std::stable_sort(pieces.begin(), pieces.end(),
+                   [](const auto& a, const auto& b) { return a.first > b.first; });
+  for (const auto& pc : pieces) p->items.push_back(pc.second);
+
+  // packed device image
+  auto& blob = p->host_blob;
+  size_t off = 0;
+  auto region = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  p->off_items = region(p->items.size() * sizeof(WorkItem));
+  p->off_qblocks = region(p->qblocks.size() * sizeof(QBlock));
+  p->off_qb_slots = region(p->qb_slots.size() * sizeof(SlotRange));
+  p->off_users = region(p->users.size() * sizeof(UserInfo));
+  p->off_row_qblock = region(p->row_qblock.size() * sizeof(int32_t));
+  p->off_new_offsets = region(p->new_offsets.size() * sizeof(int32_t));
+  p->off_start_pos = region(p->start_pos.size() * sizeof(int32_t));
+  blob.assign(off, 0);
+  auto copy = [&](size_t o, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(blob.data() + o, src, bytes);
+  };
+  copy(p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  copy(p->off_qblocks, p->qblocks.data(), p->qblocks.size() * sizeof(QBlock));
+  copy(p->off_qb_slots, p->qb_slots.data(), p->qb_slots.size() * sizeof(SlotRange));
+  copy(p->off_users, p->users.data(), p->users.size() * sizeof(UserInfo));
+  copy(p->off_row_qblock, p->row_qblock.data(), p->row_qblock.size() * sizeof(int32_t));
+  copy(p->off_new_offsets, p->new_offsets.data(), p->new_offsets.size() * sizeof(int32_t));
+  copy(p->off_start_pos, p->start_pos.data(), p->start_pos.size() * sizeof(int32_t));
+  *out = p;
+  return ok();
+}
+
+hstu_status hstu_plan_destroy(hstu_plan* p) {
+  delete p;
+  return ok();
+}
+
+hstu_status hstu_plan_get_info(const hstu_plan* p, hstu_plan_info* info) {
+  if (!p || !info) return fail(HSTU_ERR_INVALID, "hstu_plan_get_info: null argument");
+  info->n_new_total = p->n_new;
+  info->n_work_items = static_cast<int32_t>(p->items.size());
+  info->n_partial_slots = p->n_slots;
+  info->pairs = p->pairs;
+  info->meta_bytes = p->host_blob.size();
+  info->attn_workspace_bytes =
+      align256(static_cast<size_t>(p->n_slots) * kBlockQ * p->desc.head_dim * sizeof(float));
+  return ok();
+}
+
+hstu_status hstu_plan_upload(hstu_plan* p, void* d_meta, size_t bytes, hipStream_t stream) {
+  if (!p || !d_meta) return fail(HSTU_ERR_INVALID, "hstu_plan_upload: null argument");
+  if (bytes < p->host_blob.size()) return fail(HSTU_ERR_INVALID, "hstu_plan_upload: buffer too small");
+  if (reinterpret_cast<uintptr_t>(d_meta) % 256)
+    return fail(HSTU_ERR_INVALID, "hstu_plan_upload: d_meta must be 256-byte aligned");
+  hstu_status st = check_hip(hipMemcpyAsync(d_meta, p->host_blob.data(), p->host_blob.size(),
+                                            hipMemcpyHostToDevice, stream),
+                             "hstu_plan_upload");
+  if (st != HSTU_OK) return st;
+  auto* base = static_cast<unsigned char*>(d_meta);
+  p->d_meta = d_meta;
+  PlanDev& dv = p->dev;
+  dv.items = reinterpret_cast<const WorkItem*>(base + p->off_items);
+  dv.qblocks = reinterpret_cast<const QBlock*>(base + p->off_qblocks);
+  dv.qb_slots = reinterpret_cast<const SlotRange*>(base + p->off_qb_slots);
+  dv.users = reinterpret_cast<const UserInfo*>(base + p->off_users);
+  dv.row_qblock = reinterpret_cast<const int32_t*>(base + p->off_row_qblock);
+  dv.new_offsets = reinterpret_cast<const int32_t*>(base + p->off_new_offsets);
+  dv.start_pos = reinterpret_cast<const int32_t*>(base + p->off_start_pos);
+  dv.n_items = static_cast<int32_t>(p->items.size());
+  dv.n_qblocks = static_cast<int32_t>(p->qblocks.size());
+  dv.n_new = p->n_new;
+  dv.B = p->desc.B;
+  dv.H = p->desc.num_heads;
+  dv.dh = p->desc.head_dim;
+  dv.page_size = p->desc.page_size;
+  dv.max_pages = p->desc.max_pages;
+  dv.max_len = p->max_len;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// KV data movement
+// ---------------------------------------------------------------------------
+
+hstu_status kv_page_append(const hstu_kv_cache* c, int32_t layer, int32_t B,
+                           const int32_t* d_new_offsets, const int32_t* d_start_pos,
+                           const int32_t* d_page_table, int32_t max_pages, const void* k_new,
+                           const void* v_new, int64_t row_stride, int32_t n_new_total,
+                           hipStream_t stream) {
+  if (!c || !c->k_pool) return fail(HSTU_ERR_INVALID, "kv_page_append: cache without pools");
+  if (layer < 0 || layer >= c->num_layers || B < 0 || max_pages <= 0 || n_new_total < 0)
+    return fail(HSTU_ERR_INVALID, "kv_page_append: bad layer/B/max_pages/n_new_total");
+  if (row_stride < static_cast<int64_t>(c->num_heads) * c->head_dim)
+    return fail(HSTU_ERR_INVALID, "kv_page_append: row_stride smaller than a row");
+  if (n_new_total == 0) return ok();
+  if (!d_new_offsets || !d_start_pos || !d_page_table || !k_new || !v_new)
+    return fail(HSTU_ERR_INVALID, "kv_page_append: null device pointer");
+  if (row_stride % 8 != 0 || reinterpret_cast<uintptr_t>(k_new) % 16 ||
+      reinterpret_cast<uintptr_t>(v_new) % 16)
+    return fail(HSTU_ERR_INVALID, "kv_page_append: rows must be 16-byte aligned");
+  return check_hip(timed(TK_APPEND, stream, [&] { return launch_append(c->dtype, nullptr, B, d_new_offsets, d_start_pos, d_page_table,
+                                 max_pages, k_new, v_new, row_stride, n_new_total, c->k_pool,
+                                 c->v_pool, layer, c->num_pages, c->num_heads, c->head_dim,
+                                 c->page_size, stream); }),
+                   "kv_page_append");
+}
+
+hstu_status kv_page_gather(const hstu_kv_cache* c, int32_t layer, int32_t B,
+                           const int32_t* d_page_table, int32_t max_pages, const int32_t* d_kv_len,
+                           const int32_t* d_out_offsets, int32_t n_out_total, void* k_out,
+                           void* v_out, hipStream_t stream) {
+  if (!c || !c->k_pool) return fail(HSTU_ERR_INVALID, "kv_page_gather: cache without pools");
+  if (layer < 0 || layer >= c->num_layers || B < 0 || max_pages <= 0 || n_out_total < 0)
+    return fail(HSTU_ERR_INVALID, "kv_page_gather: bad layer/B/max_pages/n_out_total");
+  if (n_out_total == 0) return ok();
+  if (!d_page_table || !d_kv_len || !d_out_offsets || !k_out || !v_out)
+    return fail(HSTU_ERR_INVALID, "kv_page_gather: null device pointer");
+  return check_hip(timed(TK_GATHER, stream, [&] { return launch_gather(c->dtype, B, d_page_table, max_pages, d_kv_len, d_out_offsets,
+                                 n_out_total, k_out, v_out, c->k_pool, c->v_pool, layer,
+                                 c->num_pages, c->num_heads, c->head_dim, c->page_size, stream); }),
+                   "kv_page_gather");
+}
+
+// ---------------------------------------------------------------------------
+// attention and layer
+// ---------------------------------------------------------------------------
+
+static hstu_status check_plan(const hstu_plan* p, const char* who) {
+  if (!p) return fail(HSTU_ERR_INVALID, std::string(who) + ": null plan");
+  if (!p->d_meta) return fail(HSTU_ERR_INVALID, std::string(who) + ": plan not uploaded");
+  return HSTU_OK;
+}
+
+static hstu_status check_dtype_shape(int dtype, int dh, const char* who) {
+  if (dtype != HSTU_F32 && dtype != HSTU_BF16)
+    return fail(HSTU_ERR_INVALID, std::string(who) + ": unknown dtype");
+  if (dtype == HSTU_BF16 && dh != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": bf16 needs head_dim 128");
+  return HSTU_OK;
+}
+
+static hstu_status fill_keys(AttnLaunch& L, const hstu_plan* p, int dtype, const void* k,
+                             const void* v, int64_t kv_stride, const hstu_kv_cache* cache,
+                             int32_t layer, const int32_t* d_pt, const char* who) {
+  const int H = p->desc.num_heads, dh = p->desc.head_dim;
+  if (p->desc.page_size > 0) {
+    if (!cache || !cache->k_pool || !d_pt)
+      return fail(HSTU_ERR_INVALID, std::string(who) + ": paged plan needs a cache and page table");
+    if (cache->page_size != p->desc.page_size || cache->num_heads != H ||
+        cache->head_dim != dh || cache->dtype != dtype)
+      return fail(HSTU_ERR_INVALID, std::string(who) + ": cache geometry differs from the plan");
+    if (layer < 0 || layer >= cache->num_layers)
+      return fail(HSTU_ERR_INVALID, std::string(who) + ": bad layer");
+    L.k_pool = cache->k_pool;
+    L.v_pool = cache->v_pool;
+    L.pool_layer_offset =
+        static_cast<int64_t>(layer) * cache->num_pages * H * cache->page_size * dh;
+    L.num_pages = cache->num_pages;
+    L.page_table = d_pt;
+  } else {
+    if (!k || !v) return fail(HSTU_ERR_INVALID, std::string(who) + ": contiguous plan needs k and v");
+    if (kv_stride < static_cast<int64_t>(H) * dh || kv_stride % 8)
+      return fail(HSTU_ERR_INVALID, std::string(who) + ": bad kv_row_stride");
+    L.k = k;
+    L.v = v;
+    L.kv_stride = kv_stride;
+  }
+  return HSTU_OK;
+}
+
+hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
+  if (!a) return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null args");
+  hstu_status st = check_plan(a->plan, "hstu_attn_fwd");
+  if (st != HSTU_OK) return st;
+  const hstu_plan* p = a->plan;
+  const int H = p->desc.num_heads, dh = p->desc.head_dim;
+  if ((st = check_dtype_shape(a->dtype, dh, "hstu_attn_fwd")) != HSTU_OK) return st;
+  if (p->n_new == 0) return ok();
+  if (!a->q || !a->out || !a->rab || a->num_buckets <= 0)
+    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null q/out/rab or no buckets");
+  if (a->q_row_stride < static_cast<int64_t>(H) * dh || a->q_row_stride % 8)
+    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: bad q_row_stride");
+  hstu_plan_info info{};
+  hstu_plan_get_info(p, &info);
+  if (!a->workspace || a->workspace_bytes < info.attn_workspace_bytes)
+    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: workspace too small");
+  AttnLaunch L{};
+  L.dtype = a->dtype;
+  L.plan = p->dev;
+  L.q = a->q;
+  L.q_stride = a->q_row_stride;
+  L.rab = a->rab;
+  L.num_buckets = a->num_buckets;
+  L.partials = static_cast<float*>(a->workspace);
+  if ((st = fill_keys(L, p, a->dtype, a->k, a->v, a->kv_row_stride, a->cache, a->layer,
+                      a->d_page_table, "hstu_attn_fwd")) != HSTU_OK)
+    return st;
+  if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_attn_fwd: attention")) != HSTU_OK)
+    return st;
+  return check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, nullptr, 0, 0.f, a->out,
+                                      nullptr, stream); }),
+                   "hstu_attn_fwd: reduce");
+}
+
+namespace {
+struct LayerWs {
+  size_t xhat, uvqk, partials, g, total;
+};
+LayerWs layer_ws(const hstu_plan* p, int dtype, int d_model) {
+  const size_t n = static_cast<size_t>(p->n_new), inner = p->desc.num_heads * p->desc.head_dim;
+  LayerWs w{};
+  size_t off = 0;
+  w.xhat = off;
+  off = align256(off + n * d_model * esize(dtype) + 1);
+  w.uvqk = off;
+  off = align256(off + n * 4 * inner * esize(dtype) + 1);
+  w.partials = off;
+  off = align256(off + static_cast<size_t>(p->n_slots) * kBlockQ * p->desc.head_dim * 4 + 1);
+  w.g = off;
+  off = align256(off + n * inner * esize(dtype) + 1);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+hstu_status hstu_layer_workspace_size(const hstu_layer_args* a, size_t* bytes) {
+  if (!a || !bytes || !a->plan) return fail(HSTU_ERR_INVALID, "hstu_layer_workspace_size: null");
+  *bytes = layer_ws(a->plan, a->dtype, a->d_model).total;
+  return ok();
+}
+
+hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
+  if (!a) return fail(HSTU_ERR_INVALID, "hstu_layer_forward: null args");
+  hstu_status st = check_plan(a->plan, "hstu_layer_forward");
+  if (st != HSTU_OK) return st;
+  const hstu_plan* p = a->plan;
+  const int H = p->desc.num_heads, dh = p->desc.head_dim, inner = H * dh, d = a->d_model;
+  if ((st = check_dtype_shape(a->dtype, dh, "hstu_layer_forward")) != HSTU_OK) return st;
+  if (d <= 0 || (a->dtype == HSTU_BF16 && d % 128 != 0) || (a->dtype == HSTU_F32 && d % 4 != 0))
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "hstu_layer_forward: d_model must be a multiple of 128 (bf16) or 4 (fp32)");
+  if (!(a->eps >= 0.f)) return fail(HSTU_ERR_INVALID, "hstu_layer_forward: eps must be >= 0");
+  if (p->n_new == 0) return ok();
+  if (!a->x || !a->y || !a->w1 || !a->w2 || !a->rab || a->num_buckets <= 0)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_forward: null x/y/w1/w2/rab or no buckets");
+  const size_t xbytes = static_cast<size_t>(p->n_new) * d * esize(a->dtype);
+  {
+    auto xb = reinterpret_cast<uintptr_t>(a->x), yb = reinterpret_cast<uintptr_t>(a->y);
+    if (xb < yb + xbytes && yb < xb + xbytes)
+      return fail(HSTU_ERR_INVALID, "hstu_layer_forward: y overlaps x");
+  }
+  if (p->desc.page_size == 0) {
+    for (int32_t c : p->cached_len)
+      if (c != 0)
+        return fail(HSTU_ERR_INVALID, "hstu_layer_forward: contiguous plan with cached positions");
+  }
+  LayerWs w = layer_ws(p, a->dtype, d);
+  if (!a->workspace || a->workspace_bytes < w.total)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_forward: workspace too small");
+  if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_forward: workspace must be 256-byte aligned");
+  auto* ws = static_cast<unsigned char*>(a->workspace);
+  void* xhat = ws + w.xhat;
+  auto* uvqk = static_cast<unsigned char*>(a->uvqk_out ? a->uvqk_out : ws + w.uvqk);
+  float* partials = reinterpret_cast<float*>(ws + w.partials);
+  void* g = a->g_out ? a->g_out : ws + w.g;
+  const size_t es = esize(a->dtype);
+  const int32_t M = p->n_new;
+
+  if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_layer_norm(a->dtype, a->x, xhat, M, d, a->eps, stream); }),
+                      "hstu_layer_forward: pre-norm")) != HSTU_OK)
+    return st;
+  if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_gemm(a->dtype, 0, xhat, a->w1, uvqk, nullptr, M, 4 * inner, d, stream); }),
+                      "hstu_layer_forward: f1")) != HSTU_OK)
+    return st;
+  const void* v_new = uvqk + static_cast<size_t>(inner) * es;
+  const void* q_new = uvqk + static_cast<size_t>(2 * inner) * es;
+  const void* k_new = uvqk + static_cast<size_t>(3 * inner) * es;
+  AttnLaunch L{};
+  L.dtype = a->dtype;
+  L.plan = p->dev;
+  L.q = q_new;
+  L.q_stride = 4 * inner;
+  L.rab = a->rab;
+  L.num_buckets = a->num_buckets;
+  L.partials = partials;
+  if (p->desc.page_size > 0) {
+    if ((st = fill_keys(L, p, a->dtype, nullptr, nullptr, 0, a->cache, a->layer, a->d_page_table,
+                        "hstu_layer_forward")) != HSTU_OK)
+      return st;
+    const hstu_kv_cache* c = a->cache;
+    if ((st = check_hip(timed(TK_APPEND, stream, [&] { return launch_append(a->dtype, &p->dev, p->desc.B, p->dev.new_offsets,
+                                      p->dev.start_pos, a->d_page_table, p->desc.max_pages, k_new,
+                                      v_new, 4 * inner, M, c->k_pool, c->v_pool, a->layer,
+                                      c->num_pages, H, dh, c->page_size, stream); }),
+                        "hstu_layer_forward: append")) != HSTU_OK)
+      return st;
+  } else {
+    if ((st = fill_keys(L, p, a->dtype, k_new, v_new, 4 * inner, nullptr, 0, nullptr,
+                        "hstu_layer_forward")) != HSTU_OK)
+      return st;
+  }
+  if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_layer_forward: attention")) != HSTU_OK)
+    return st;
+  if ((st = check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, partials, uvqk, 4 * inner, a->eps,
+                                         a->o_out, g, stream); }),
+                      "hstu_layer_forward: LayerNorm gate")) != HSTU_OK)
+    return st;
+  return check_hip(timed(TK_F2, stream, [&] { return launch_gemm(a->dtype, 1, g, a->w2, a->y, a->x, M, d, inner, stream); }),
+                   "hstu_layer_forward: f2");
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// Internal declarations of libhstu: error state, the request plan's device
+// records, and the kernel launchers the ABI layer calls.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/hstu.h"
+
+namespace hstu {
+
+// ---- error reporting ------------------------------------------------------
+hstu_status fail(hstu_status st, const std::string& msg);
+hstu_status ok();
+hstu_status check_hip(hipError_t e, const char* what);
+
+// ---- tiling constants shared by the plan and the attention kernels --------
+constexpr int kBlockQ = 128;  // queries per attention work item (4 waves x 32)
+constexpr int kTileK = 64;    // keys per staged K/V tile
+constexpr int kMaxPos = 65535;
+
+// One attention work item: a block of up to kBlockQ queries of one user and
+// head, over the key tiles [tile_begin, tile_end) of that user.  Its result
+// (unnormalised sum over those keys) goes to partial slot `slot`.
+struct WorkItem {
+  int32_t user, head, qblock, tile_begin, tile_end, slot, pad0, pad1;
+};
+
+// The partial slots of one (q-block, head): consecutive, in key order.
+struct SlotRange {
+  int32_t first, count;
+};
+
+// A block of up to kBlockQ consecutive new tokens of one user.
+struct QBlock {
+  int32_t user, row0, count, pos0;
+};
+
+// Per-user scalars the kernels read.
+struct UserInfo {
+  int32_t q_row0;     // first new-token row
+  int32_t n_new;      // t_u
+  int32_t start;      // c_u (position of the first new token)
+  int32_t kv_len;     // L_u = c_u + t_u
+  int32_t hist;       // L_u - T_u
+  int32_t kv_row0;    // contiguous mode: first key row
+  float inv_n;        // 1 / n_u
+  float pad;
+};
+
+// Device view of an uploaded plan (all pointers into the caller's d_meta).
+struct PlanDev {
+  const WorkItem* items;
+  const QBlock* qblocks;
+  const SlotRange* qb_slots;  // [n_qblocks][H]
+  const UserInfo* users;
+  const int32_t* row_qblock;  // [n_new]: q-block of each new-token row
+  const int32_t* new_offsets; // [B+1]
+  const int32_t* start_pos;   // [B]
+  int32_t n_items, n_qblocks, n_new, B, H, dh, page_size, max_pages, max_len;
+};
+
+}  // namespace hstu
+
+struct hstu_plan {
+  hstu_batch_desc desc{};
+  std::vector<int32_t> new_len, cached_len, n_targets;
+  std::vector<float> norm_n;
+  std::vector<hstu::WorkItem> items;
+  std::vector<hstu::QBlock> qblocks;
+  std::vector<hstu::SlotRange> qb_slots;
+  std::vector<hstu::UserInfo> users;
+  std::vector<int32_t> row_qblock, new_offsets, start_pos;
+  int32_t n_slots = 0, n_new = 0, max_len = 0;
+  int64_t pairs = 0;
+  std::vector<unsigned char> host_blob;  // packed image of the device metadata
+  size_t off_items = 0, off_qblocks = 0, off_qb_slots = 0, off_users = 0, off_row_qblock = 0,
+         off_new_offsets = 0, off_start_pos = 0;
+  void* d_meta = nullptr;  // set by hstu_plan_upload
+  hstu::PlanDev dev{};
+};
+
+struct hstu_kv_cache {
+  struct User {
+    int32_t len = 0;
+    int64_t tick = 0;
+    std::vector<int32_t> pages;
+  };
+  int32_t num_layers = 0, num_heads = 0, head_dim = 0, page_size = 0, num_pages = 0, dtype = 0;
+  void* k_pool = nullptr;
+  void* v_pool = nullptr;
+  int64_t tick = 0;
+  std::deque<int32_t> free_q;
+  std::unordered_map<int64_t, User> users;
+};
+
+namespace hstu {
+
+// ---- optional event timing of launches (hstu_timing_*) ---------------------
+enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_COUNT };
+// Brackets one launch: records a start event now and an end event when the
+// returned guard's end() is called (both on stream s), if timing is enabled.
+struct TimedLaunch {
+  TimedLaunch(TimedKernel k, hipStream_t s);
+  void end();
+  int kernel;
+  hipStream_t stream;
+  void* start_ev;
+};
+
+// ---- kernel launchers (kernels/*.hip) -------------------------------------
+// All take device pointers and enqueue on `s`; they return the launch status.
+hipError_t launch_append(int dtype, const PlanDev* plan_or_null, int32_t B,
+                         const int32_t* d_new_offsets, const int32_t* d_start_pos,
+                         const int32_t* d_page_table, int32_t max_pages, const void* k_new,
+                         const void* v_new, int64_t row_stride, int32_t n_new_total, void* k_pool,
+                         void* v_pool, int32_t layer, int32_t num_pages, int32_t H, int32_t dh,
+                         int32_t page_size, hipStream_t s);
+hipError_t launch_gather(int dtype, int32_t B, const int32_t* d_page_table, int32_t max_pages,
+                         const int32_t* d_kv_len, const int32_t* d_out_offsets, int32_t n_out_total,
+                         void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                         int32_t layer, int32_t num_pages, int32_t H, int32_t dh, int32_t page_size,
+                         hipStream_t s);
+
+struct AttnLaunch {
+  int dtype;
+  PlanDev plan;
+  const void* q;
+  int64_t q_stride;
+  // contiguous keys
+  const void* k;
+  const void* v;
+  int64_t kv_stride;
+  // paged keys
+  const void* k_pool;
+  const void* v_pool;
+  int64_t pool_layer_offset;  // elements: layer * num_pages * H * page_size * dh
+  int32_t num_pages;
+  const int32_t* page_table;
+  const float* rab;
+  int32_t num_buckets;
+  float* partials;  // [n_slots][kBlockQ][dh]
+};
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+
+// Sums each row's partial slots in key order, scales by 1/n_u; then either
+// writes o (fp32) and/or g = LayerNorm(o) * U (dtype).
+hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials,
+                              const void* u, int64_t u_stride, float eps, float* o_out,
+                              void* g_out, hipStream_t s);
+
+// y = LayerNorm(x) rows (no affine) -> xhat (dtype)
+hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows, int32_t cols,
+                             float eps, hipStream_t s);
+
+// C[M][N] = epilogue(A[M][K] . B[K][N]); epilogue 0: SiLU, 1: + residual R[M][N]
+hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
+                       const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s);
+
+}  // namespace hstu

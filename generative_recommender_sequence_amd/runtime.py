@@ -1,0 +1,326 @@
+"""Drive HSTU requests through libhstu with torch device memory and streams.
+
+A request ("Deploying an HSTU Generative Recommender with NVIDIA
+Dynamo-Triton", KV cache section): look the users up in the paged KV table,
+evict least-recently-used users if pages are short, allocate room for the new
+tokens, then run the layer stack on the new tokens only; every layer appends
+its K/V of the new tokens and its attention reads cached history straight from
+the pages.  Without a cache the same stack runs on contiguous K/V.
+
+torch only allocates device buffers and supplies the stream; every arithmetic
+step is a libhstu kernel.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import hstu
+from .hstu import HSTU_BF16, HSTU_F32
+
+
+def tdtype(dtype: int) -> torch.dtype:
+    return torch.bfloat16 if dtype == HSTU_BF16 else torch.float32
+
+
+def dtype_code(name: str) -> int:
+    return HSTU_BF16 if name == "bf16" else HSTU_F32
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("libhstu needs a GPU (gfx950); none is visible")
+    hstu.lib()
+
+
+class Model:
+    """Device copies of a stack's weights: W1 [d][4*H*dh], W2 [H*dh][d] in the
+    compute dtype, rab [num_buckets] fp32, per layer."""
+
+    def __init__(self, layers, dtype: int, num_heads: int, head_dim: int, d_model: int,
+                 eps: float = 1e-5, device="cuda"):
+        self.dtype, self.num_heads, self.head_dim, self.d_model, self.eps = dtype, num_heads, head_dim, d_model, eps
+        t = tdtype(dtype)
+        self.w1 = [torch.from_numpy(np.ascontiguousarray(lw.w1)).to(device=device, dtype=t) for lw in layers]
+        self.w2 = [torch.from_numpy(np.ascontiguousarray(lw.w2)).to(device=device, dtype=t) for lw in layers]
+        self.rab = [torch.from_numpy(np.ascontiguousarray(lw.rab, dtype=np.float32)).to(device) for lw in layers]
+
+    @property
+    def num_layers(self) -> int:
+        return len(self.w1)
+
+
+class PagedCache:
+    """K/V pools [layers][pages][H][P][dh] in device memory plus the library's
+    host metadata handle."""
+
+    def __init__(self, num_layers, num_heads, head_dim, page_size, num_pages, dtype: int,
+                 free_order=None, device="cuda", zero=True):
+        n = num_layers * num_pages * num_heads * page_size * head_dim
+        alloc = torch.zeros if zero else torch.empty
+        self.k_pool = alloc(max(n, 1), dtype=tdtype(dtype), device=device)
+        self.v_pool = alloc(max(n, 1), dtype=tdtype(dtype), device=device)
+        self.num_layers, self.num_heads, self.head_dim = num_layers, num_heads, head_dim
+        self.page_size, self.num_pages, self.dtype = page_size, num_pages, dtype
+        self.h = hstu.kv_cache_create(num_layers, num_heads, head_dim, page_size, num_pages, dtype,
+                                      self.k_pool.data_ptr(), self.v_pool.data_ptr(), free_order)
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            hstu.lib().kv_cache_destroy(self.h)
+            self.h = None
+
+    def pages_needed(self, cached_len, n_new) -> int:
+        P = self.page_size
+        return int(sum(-(-(c + t) // P) - (-(-c // P)) for c, t in zip(cached_len, n_new)))
+
+
+@dataclass
+class Request:
+    users: np.ndarray
+    new_len: np.ndarray
+    cached_len: np.ndarray
+    n_targets: np.ndarray
+    norm_n: np.ndarray
+    kv_len: np.ndarray
+    plan: int
+    info: hstu.hstu_plan_info
+    meta: torch.Tensor
+    page_table: Optional[torch.Tensor]
+    max_pages: int
+    evicted: np.ndarray
+    num_heads: int = 1
+    head_dim: int = 128
+
+    def close(self):
+        if self.plan:
+            hstu.hstu_plan_destroy(self.plan)
+            self.plan = 0
+
+
+def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None, max_pages: int = 0,
+            num_heads: int = 1, head_dim: int = 128, device="cuda", stream=None) -> Request:
+    """Host cache operations (lookup, LRU eviction, allocation), page-table
+    upload, and the request plan, uploaded."""
+    users = np.asarray(users, np.int64)
+    new_len = np.asarray(new_len, np.int32)
+    n_targets = np.asarray(n_targets, np.int32)
+    s = stream_handle(stream)
+    evicted = np.zeros(0, np.int64)
+    if cache is not None:
+        cached = hstu.kv_lookup(cache.h, users)
+        need = cache.pages_needed(cached, new_len)
+        if hstu.kv_free_pages(cache.h) < need:
+            evicted = hstu.kv_evict_lru(cache.h, need, users)
+        pt, kv_len = hstu.kv_page_alloc(cache.h, users, new_len, max_pages)
+        d_pt = torch.from_numpy(pt).to(device)
+        page_size, num_heads, head_dim = cache.page_size, cache.num_heads, cache.head_dim
+    else:
+        cached = np.zeros(len(users), np.int32)
+        kv_len = new_len.copy()
+        d_pt, page_size, max_pages = None, 0, 0
+    nn = (cached + new_len).astype(np.float32) if norm_n is None else np.asarray(norm_n, np.float32)
+    plan = hstu.hstu_plan_create(num_heads, head_dim, new_len, cached, n_targets, nn, page_size, max_pages)
+    info = hstu.hstu_plan_get_info(plan)
+    meta = torch.empty(max(int(info.meta_bytes), 256), dtype=torch.uint8, device=device)
+    hstu.hstu_plan_upload(plan, meta.data_ptr(), meta.numel(), s)
+    return Request(users, new_len, np.asarray(cached, np.int32), n_targets, nn, np.asarray(kv_len, np.int32),
+                   plan, info, meta, d_pt, max_pages, evicted, num_heads, head_dim)
+
+
+def layer_args(model: Model, req: Request, li: int, x: torch.Tensor, y: torch.Tensor,
+               cache: Optional[PagedCache], workspace: Optional[torch.Tensor] = None,
+               taps: Optional[dict] = None) -> hstu.hstu_layer_args:
+    a = hstu.hstu_layer_args()
+    a.dtype = model.dtype
+    a.d_model = model.d_model
+    a.eps = model.eps
+    a.plan = req.plan
+    a.x = x.data_ptr()
+    a.y = y.data_ptr()
+    a.w1 = model.w1[li].data_ptr()
+    a.w2 = model.w2[li].data_ptr()
+    a.rab = model.rab[li].data_ptr()
+    a.num_buckets = model.rab[li].numel()
+    if cache is not None:
+        a.cache = cache.h
+        a.layer = li
+        a.d_page_table = req.page_table.data_ptr()
+    if taps:
+        a.uvqk_out = taps["uvqk"].data_ptr() if "uvqk" in taps else None
+        a.o_out = taps["o"].data_ptr() if "o" in taps else None
+        a.g_out = taps["g"].data_ptr() if "g" in taps else None
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel()
+    return a
+
+
+def workspace_for(model: Model, req: Request, device="cuda") -> torch.Tensor:
+    a = hstu.hstu_layer_args()
+    a.dtype, a.d_model, a.plan = model.dtype, model.d_model, req.plan
+    n = hstu.hstu_layer_workspace_size(a)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def forward(model: Model, req: Request, x: torch.Tensor, cache: Optional[PagedCache],
+            workspace: Optional[torch.Tensor] = None, layers: Optional[Sequence[int]] = None,
+            taps: Optional[List[dict]] = None, stream=None) -> torch.Tensor:
+    """Runs the stack on the new tokens x [N_new, d]; returns the last layer's y."""
+    s = stream_handle(stream)
+    if workspace is None:
+        workspace = workspace_for(model, req, x.device)
+    layers = range(model.num_layers) if layers is None else layers
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    cur = x
+    for k, li in enumerate(layers):
+        out = bufs[k % 2]
+        a = layer_args(model, req, li, cur, out, cache, workspace, taps[k] if taps else None)
+        hstu.hstu_layer_forward(a, s)
+        cur = out
+    return cur
+
+
+def attention(req: Request, q: torch.Tensor, q_row_stride: int, rab: torch.Tensor, dtype: int,
+              k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, kv_row_stride: int = 0,
+              cache: Optional[PagedCache] = None, layer: int = 0, stream=None) -> torch.Tensor:
+    """hstu_attn_fwd: o [N_new, H*dh] fp32 (includes 1/n)."""
+    s = stream_handle(stream)
+    H, dh = req.num_heads, req.head_dim
+    out = torch.empty((int(req.info.n_new_total), H * dh), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(int(req.info.attn_workspace_bytes), 256), dtype=torch.uint8, device=q.device)
+    a = hstu.hstu_attn_args()
+    a.dtype = dtype
+    a.plan = req.plan
+    a.q = q.data_ptr()
+    a.q_row_stride = q_row_stride
+    if cache is not None:
+        a.cache = cache.h
+        a.layer = layer
+        a.d_page_table = req.page_table.data_ptr()
+    else:
+        a.k, a.v, a.kv_row_stride = k.data_ptr(), v.data_ptr(), kv_row_stride
+    a.rab = rab.data_ptr()
+    a.num_buckets = rab.numel()
+    a.out = out.data_ptr()
+    a.workspace = ws.data_ptr()
+    a.workspace_bytes = ws.numel()
+    hstu.hstu_attn_fwd(a, s)
+    return out
+
+
+def prepare_attn(cache, users, new_len, n_targets, norm_n, max_pages, num_heads, head_dim, cached_len=None,
+                 device="cuda"):
+    """A plan for hstu_attn_fwd alone.  With a cache the page table comes from
+    the cache (positions must already be there); without one, cached_len gives
+    the contiguous prefix length of each user."""
+    new_len = np.asarray(new_len, np.int32)
+    n_targets = np.asarray(n_targets, np.int32)
+    s = stream_handle()
+    if cache is not None:
+        pt, kv_len = hstu.kv_page_table(cache.h, users, max_pages)
+        cached = (kv_len - new_len).astype(np.int32)
+        d_pt = torch.from_numpy(pt).to(device)
+        page_size = cache.page_size
+    else:
+        cached = np.zeros(len(new_len), np.int32) if cached_len is None else np.asarray(cached_len, np.int32)
+        kv_len = cached + new_len
+        d_pt, page_size, max_pages = None, 0, 0
+    nn = kv_len.astype(np.float32) if norm_n is None else np.asarray(norm_n, np.float32)
+    plan = hstu.hstu_plan_create(num_heads, head_dim, new_len, cached, n_targets, nn, page_size, max_pages)
+    info = hstu.hstu_plan_get_info(plan)
+    meta = torch.empty(max(int(info.meta_bytes), 256), dtype=torch.uint8, device=device)
+    hstu.hstu_plan_upload(plan, meta.data_ptr(), meta.numel(), s)
+    return Request(np.asarray(users, np.int64), new_len, cached, n_targets, nn, np.asarray(kv_len, np.int32),
+                   plan, info, meta, d_pt, max_pages, np.zeros(0, np.int64), num_heads, head_dim)
+
+
+# ---------------------------------------------------------------------------
+# a workload's serving scenario: weights, pool, pre-filled cache, request
+# ---------------------------------------------------------------------------
+
+def _ceil(a, b):
+    return -(-int(a) // int(b))
+
+
+class Scenario:
+    """Device state for one synthetic workload.
+
+    cache "none":  every request recomputes each user's whole sequence.
+    cache "hit":   each user's history is pre-filled into the pages (placed by
+                   the workload's page permutation); the request computes and
+                   appends only the candidates.
+    cache "mixed": hit users and stale users are pre-filled; the request runs
+                   hit users on their candidates and the others on their whole
+                   sequence, evicting least-recently-used stale users.
+    Pre-fill uses the final normaliser n_u = history + candidates, so a cached
+    prefix plus the appended candidates equals a full recompute."""
+
+    def __init__(self, w, device="cuda"):
+        self.w, self.cfg, self.device = w, w.cfg, device
+        cfg = w.cfg
+        self.dtype = dtype_code(cfg.dtype)
+        self.model = Model(w.layers, self.dtype, cfg.num_heads, cfg.head_dim, cfg.d_model, cfg.eps, device)
+        L = w.hist_len + w.n_targets
+        lens = list(L) + [int(h) + cfg.n_targets for h in w.stale_hist_len]
+        self.max_pages = max(1, max(_ceil(l, cfg.page_size) for l in lens)) if lens else 1
+        self.cache = None
+        if cfg.cache != "none":
+            self.cache = PagedCache(cfg.num_layers, cfg.num_heads, cfg.head_dim, cfg.page_size, w.num_pages,
+                                    self.dtype, w.page_perm, device)
+        self.snapshot = None
+
+    def _x(self, rows) -> torch.Tensor:
+        a = np.concatenate(rows, axis=0) if rows else np.zeros((0, self.cfg.d_model), np.float32)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=self.device, dtype=tdtype(self.dtype))
+
+    def prefill(self):
+        """Pre-fills the cached users' histories (in the workload's pre-fill order)."""
+        w, cfg = self.w, self.cfg
+        if self.cache is None:
+            return
+        cached_users = [(w.user_ids[b], w.x[b][:w.hist_len[b]], int(w.hist_len[b] + w.n_targets[b]))
+                        for b in range(cfg.batch) if w.hit[b]]
+        cached_users += [(w.stale_ids[s], w.x_stale[s], int(w.stale_hist_len[s] + cfg.n_targets))
+                         for s in range(len(w.stale_ids))]
+        order = [cached_users[i] for i in w.prefill_order]
+        if order:
+            users = [u for u, _, _ in order]
+            new_len = [len(x) for _, x, _ in order]
+            req = prepare(self.cache, users, new_len, [0] * len(users), [n for _, _, n in order],
+                          self.max_pages, device=self.device)
+            forward(self.model, req, self._x([x for _, x, _ in order]), self.cache)
+            torch.cuda.synchronize()
+            req.close()
+        self.snapshot = hstu.kv_state_dump(self.cache.h)
+
+    def request_inputs(self):
+        """(users, new_len, n_targets, norm_n, list of new-token rows) in batch order."""
+        w = self.w
+        users, new_len, rows = [], [], []
+        for b in range(self.cfg.batch):
+            x = w.x[b]
+            start = int(w.hist_len[b]) if w.hit[b] else 0
+            users.append(int(w.user_ids[b]))
+            new_len.append(len(x) - start)
+            rows.append(x[start:])
+        norm_n = (w.hist_len + w.n_targets).astype(np.float32)
+        return users, new_len, list(w.n_targets), norm_n, rows
+
+    def restore(self):
+        if self.cache is not None and self.snapshot is not None:
+            hstu.kv_state_load(self.cache.h, self.snapshot)
+
+    def make_request(self, x_rows=None):
+        users, new_len, n_targets, norm_n, rows = self.request_inputs()
+        req = prepare(self.cache, users, new_len, n_targets, norm_n, self.max_pages, self.cfg.num_heads,
+                      self.cfg.head_dim, self.device)
+        return req, self._x(rows if x_rows is None else x_rows)

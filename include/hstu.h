@@ -1,0 +1,282 @@
+/*
+ * hstu.h - C ABI of the MI355X (gfx950) HSTU block forward with a paged KV cache.
+ *
+ * Sources this interface follows:
+ *  [GR]  "How Generative Recommenders Are Redefining RecSys at Scale", section
+ *        HSTU: attention aggregation with SiLU-based weighting in place of the
+ *        softmax, a relative attention bias, and elementwise gating before the
+ *        output projection; per-user sequences of interleaved events.
+ *  [DT]  "Deploying an HSTU Generative Recommender with NVIDIA Dynamo-Triton"
+ *        (and its French and German renderings), section on the KV cache: a
+ *        paged KV data table in GPU memory supporting lookup, allocation,
+ *        append and eviction, with older users evicted LRU-style when space is
+ *        tight; cache-aware operations for lookup, allocation and appending;
+ *        the HSTU attention kernel consumes the cached data directly so stable
+ *        history is not recomputed; benchmark details: hidden size 512, 4 heads,
+ *        BF16 weights, 3- and 8-layer models, batch 8.
+ *
+ * One HSTU layer, for the new tokens of each user u (positions c_u .. L_u-1
+ * of a sequence whose first c_u positions are already cached):
+ *     x^        = LayerNorm(x)                 over d_model, biased variance, no affine
+ *     [U|V|Q|K] = SiLU(x^ . W1)                W1 [d_model][4*H*dh], chunks U,V,Q,K in
+ *                                              that order, head-major inside a chunk
+ *     o_i       = (1/n_u) * sum_{j in M(i)} SiLU(q_i . k_j + rab[b(i - j)]) * v_j   (per head)
+ *     g         = LayerNorm(o) * U             over all H*dh values of a token, no affine
+ *     y         = x + g . W2                   W2 [H*dh][d_model]
+ *   M(i) = { j <= i } when i < L_u - T_u (history), else { j < L_u - T_u } u { i }
+ *   (the last T_u positions are candidates: they see the whole history and
+ *   themselves, not each other).  b(delta) = min(num_buckets - 1,
+ *   floor(4 * log2(1 + delta))), one rab table per layer shared by the heads.
+ *
+ * Conventions
+ *  - Every call returns an hstu_status; no exception crosses the ABI.  On an
+ *    error hstu_last_error() (thread-local, valid until the next call on the
+ *    same thread) describes it.
+ *  - "host" pointers are CPU memory read during the call; "device" pointers
+ *    are GPU memory owned by the caller.  The library never allocates device
+ *    memory: every device buffer (inputs, outputs, weights, pools, page
+ *    tables, plan metadata, workspace) belongs to the caller.
+ *  - Device work is enqueued asynchronously on the caller's stream.  Host
+ *    metadata calls (kv_*, hstu_plan_*) are synchronous and not thread-safe
+ *    per handle; the caller serialises them.
+ *  - Element types: HSTU_BF16 (bfloat16 storage, fp32 accumulation) or
+ *    HSTU_F32.  Matrices are row-major.
+ *  - Sequence positions must stay below 65536; bf16 needs head_dim 128;
+ *    fp32 supports head_dim 32, 64 or 128.  Other shapes: HSTU_ERR_UNSUPPORTED.
+ */
+#ifndef HSTU_H
+#define HSTU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID = 1,      /* bad argument; nothing changed */
+  HSTU_ERR_NO_SPACE = 2,     /* not enough free pages; nothing changed */
+  HSTU_ERR_UNKNOWN_USER = 3, /* user not in the cache */
+  HSTU_ERR_DEVICE = 4,       /* a HIP call or kernel launch failed */
+  HSTU_ERR_UNSUPPORTED = 5   /* valid, but a shape this build has no kernel for */
+} hstu_status;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+
+/* Description of the last error on this thread ("" if none). */
+const char *hstu_last_error(void);
+/* ABI version of this header (currently 1). */
+int32_t hstu_abi_version(void);
+
+/* ======================================================================== */
+/* KV cache  [DT]: paged table with lookup, allocation, append, LRU eviction */
+/* ======================================================================== */
+
+typedef struct hstu_kv_cache hstu_kv_cache;
+
+typedef struct {
+  int32_t num_layers, num_heads, head_dim, page_size, num_pages;
+  int32_t dtype;    /* hstu_dtype of the pools */
+  /* device, each [num_layers][num_pages][num_heads][page_size][head_dim];
+   * both NULL for a metadata-only cache (kv_page_append/gather then fail). */
+  void *k_pool;
+  void *v_pool;
+  /* host, a permutation of 0..num_pages-1 giving the initial free-queue
+   * order, or NULL for 0, 1, 2, ... (copied during the call) */
+  const int32_t *initial_free_order;
+} hstu_kv_cache_desc;
+
+/* Creates the host metadata of a cache over caller-owned pools. */
+hstu_status kv_cache_create(const hstu_kv_cache_desc *desc, hstu_kv_cache **out);
+hstu_status kv_cache_destroy(hstu_kv_cache *cache);
+
+/* lookup [DT]: cached_len[b] (host out) = positions of users[b] already
+ * cached, 0 for a user not in the cache.  Each present user gets a fresh LRU
+ * tick (global counter, pre-incremented, batch order).  users: host [B],
+ * distinct (duplicates: INVALID). */
+hstu_status kv_lookup(hstu_kv_cache *cache, const int64_t *users, int32_t B, int32_t *cached_len);
+
+/* eviction [DT]: if fewer than pages_needed pages are free, evicts whole users
+ * in ascending (tick, id) order, never one listed in pinned (host
+ * [n_pinned]), until free >= pages_needed.  Freed pages join the tail of the
+ * free queue in logical order.  evicted (host out, capacity cap) receives the
+ * evicted ids in eviction order, *n_evicted their count.  If the request
+ * cannot be met: NO_SPACE, nothing changed; if cap is too small: INVALID,
+ * nothing changed. */
+hstu_status kv_evict_lru(hstu_kv_cache *cache, int32_t pages_needed, const int64_t *pinned,
+                         int32_t n_pinned, int64_t *evicted, int32_t cap, int32_t *n_evicted);
+
+/* allocation [DT]: reserves room for n_new[b] (host [B]) more positions of
+ * users[b] (host [B], distinct; a user not yet cached is created).  Pages
+ * come from the head of the free queue, users in batch order; a user's last
+ * partial page is filled first, so a user of length L owns ceil(L/P) pages.
+ * Each user gets a fresh tick.  Outputs (host): page_table [B][max_pages]
+ * (the user's physical pages in logical order, then -1), kv_len [B] (the new
+ * length).  All-or-nothing: NO_SPACE if pages are short, INVALID if a user
+ * would need more than max_pages pages; nothing changed in either case. */
+hstu_status kv_page_alloc(hstu_kv_cache *cache, const int64_t *users, const int32_t *n_new, int32_t B,
+                          int32_t *page_table, int32_t max_pages, int32_t *kv_len);
+
+/* Frees the whole pages of `user` past new_len (0 <= new_len <= length) and
+ * sets its length; the tick is unchanged.  UNKNOWN_USER / INVALID otherwise. */
+hstu_status kv_truncate(hstu_kv_cache *cache, int64_t user, int32_t new_len);
+
+/* Number of free pages (host out). */
+hstu_status kv_free_pages(const hstu_kv_cache *cache, int32_t *n_free);
+
+/* Page table of users (host [B]) as kv_page_alloc would return it, without
+ * touching ticks; UNKNOWN_USER if one is absent. */
+hstu_status kv_page_table(const hstu_kv_cache *cache, const int64_t *users, int32_t B,
+                          int32_t *page_table, int32_t max_pages, int32_t *kv_len);
+
+/* Canonical state bytes (little endian): u32 0x564B5348, u32 1, i32 num_pages,
+ * i32 page_size, i64 tick, i32 n_users, i32 n_free; per user in ascending id:
+ * i64 id, i32 len, i64 tick, i32 n_pages, i32 pages[n_pages]; then i32
+ * free[n_free] from head to tail.  *needed = size; writes only if cap >= size. */
+hstu_status kv_state_dump(const hstu_kv_cache *cache, void *buf, size_t cap, size_t *needed);
+/* Replaces the metadata with a dump of a cache of the same geometry (the
+ * pools are untouched).  INVALID (nothing changed) if inconsistent. */
+hstu_status kv_state_load(hstu_kv_cache *cache, const void *buf, size_t len);
+
+/* append [DT]: copies the K and V rows of the new tokens into their pages of
+ * `layer`.  User b's new rows are d_new_offsets[b] .. d_new_offsets[b+1]-1
+ * (device int32 [B+1]) of k_new / v_new (device, row r at r*row_stride
+ * elements, H*dh values head-major); they go to positions d_start_pos[b]
+ * (device int32 [B]) onwards, through d_page_table (device int32
+ * [B][max_pages]).  n_new_total = d_new_offsets[B] (host copy, sizes the
+ * launch).  Byte-exact copy. */
+hstu_status kv_page_append(const hstu_kv_cache *cache, int32_t layer, int32_t B,
+                           const int32_t *d_new_offsets, const int32_t *d_start_pos,
+                           const int32_t *d_page_table, int32_t max_pages, const void *k_new,
+                           const void *v_new, int64_t row_stride, int32_t n_new_total,
+                           hipStream_t stream);
+
+/* gather: copies positions 0..d_kv_len[b]-1 of each user from the pages of
+ * `layer` to contiguous rows d_out_offsets[b].. of k_out / v_out (device,
+ * [n_out_total][H*dh]).  Byte-exact copy. */
+hstu_status kv_page_gather(const hstu_kv_cache *cache, int32_t layer, int32_t B,
+                           const int32_t *d_page_table, int32_t max_pages, const int32_t *d_kv_len,
+                           const int32_t *d_out_offsets, int32_t n_out_total, void *k_out,
+                           void *v_out, hipStream_t stream);
+
+/* ======================================================================== */
+/* Request plan: the jagged batch of one request, scheduled once on the host */
+/* and reused by every layer                                                 */
+/* ======================================================================== */
+
+typedef struct hstu_plan hstu_plan;
+
+typedef struct {
+  int32_t B, num_heads, head_dim;
+  const int32_t *new_len;    /* host [B] t_u >= 0: tokens computed this request */
+  const int32_t *cached_len; /* host [B] c_u >= 0: positions already cached (0 without a cache) */
+  const int32_t *n_targets;  /* host [B] T_u: the last T_u positions of c_u + t_u are candidates */
+  const float *norm_n;       /* host [B] n_u (> 0 where t_u > 0), or NULL for n_u = c_u + t_u */
+  /* K/V addressing: page_size > 0 reads keys through a page table of
+   * max_pages entries per user; page_size == 0 reads contiguous rows. */
+  int32_t page_size, max_pages;
+} hstu_batch_desc;
+
+typedef struct {
+  int32_t n_new_total;       /* sum t_u */
+  int32_t n_work_items;      /* attention work items (query block x head x key range) */
+  int32_t n_partial_slots;   /* fp32 [128][head_dim] partial tiles */
+  int64_t pairs;             /* unmasked (query, key) pairs per head */
+  size_t meta_bytes;         /* device bytes hstu_plan_upload needs */
+  size_t attn_workspace_bytes;
+} hstu_plan_info;
+
+hstu_status hstu_plan_create(const hstu_batch_desc *desc, hstu_plan **out);
+hstu_status hstu_plan_destroy(hstu_plan *plan);
+hstu_status hstu_plan_get_info(const hstu_plan *plan, hstu_plan_info *info);
+/* Copies the schedule to d_meta (device, >= meta_bytes, 256-byte aligned) on
+ * `stream`; the plan then refers to d_meta, which must outlive its use.  The
+ * plan's host copy stays valid until hstu_plan_destroy. */
+hstu_status hstu_plan_upload(hstu_plan *plan, void *d_meta, size_t bytes, hipStream_t stream);
+
+/* ======================================================================== */
+/* Attention [GR]: o = (1/n) sum SiLU(q.k + rab) v over the mask             */
+/* ======================================================================== */
+
+typedef struct {
+  int32_t dtype;            /* hstu_dtype of q, k, v */
+  const hstu_plan *plan;    /* uploaded */
+  /* device: query row r (= new token r of the jagged batch) head h at
+   * q + r*q_row_stride + h*head_dim */
+  const void *q;
+  int64_t q_row_stride;
+  /* contiguous keys (plan page_size == 0): user u position j is row
+   * sum_{w<u}(c_w + t_w) + j of k and v (row stride kv_row_stride) */
+  const void *k, *v;
+  int64_t kv_row_stride;
+  /* paged keys (plan page_size > 0): the cache's pools at `layer`, through
+   * d_page_table (device int32 [B][max_pages]); must already hold every
+   * position 0..c_u+t_u-1 (append first) */
+  const hstu_kv_cache *cache;
+  int32_t layer;
+  const int32_t *d_page_table;
+  const float *rab;         /* device fp32 [num_buckets] */
+  int32_t num_buckets;
+  float *out;               /* device fp32 [n_new_total][H*head_dim] */
+  void *workspace;          /* device, >= attn_workspace_bytes, 256-aligned */
+  size_t workspace_bytes;
+} hstu_attn_args;
+
+hstu_status hstu_attn_fwd(const hstu_attn_args *args, hipStream_t stream);
+
+/* ======================================================================== */
+/* One HSTU layer [GR]: pre-norm, f1 + SiLU, (append), attention,            */
+/* LayerNorm(o) * U, f2 + residual                                           */
+/* ======================================================================== */
+
+typedef struct {
+  int32_t dtype;            /* hstu_dtype of x, y, w1, w2, and the pools */
+  int32_t d_model;          /* multiple of 128 (bf16) or 4 (fp32) */
+  float eps;                /* both LayerNorms */
+  const hstu_plan *plan;    /* uploaded */
+  const void *x;            /* device [n_new_total][d_model] */
+  void *y;                  /* device [n_new_total][d_model], must not overlap x */
+  const void *w1;           /* device [d_model][4*H*head_dim] */
+  const void *w2;           /* device [H*head_dim][d_model] */
+  const float *rab;         /* device fp32 [num_buckets] */
+  int32_t num_buckets;
+  /* paged (plan page_size > 0): K/V of the new tokens are appended to
+   * `cache` at `layer` and the attention reads every key from the pages.
+   * Contiguous (page_size == 0): every c_u must be 0. */
+  const hstu_kv_cache *cache;
+  int32_t layer;
+  const int32_t *d_page_table;
+  void *workspace;          /* device, >= hstu_layer_workspace_size, 256-aligned */
+  size_t workspace_bytes;
+  /* optional device taps (NULL = skip): [U|V|Q|K] after SiLU
+   * [n_new_total][4*H*dh] (dtype), o [n_new_total][H*dh] fp32, g (dtype) */
+  void *uvqk_out;
+  float *o_out;
+  void *g_out;
+} hstu_layer_args;
+
+hstu_status hstu_layer_workspace_size(const hstu_layer_args *args, size_t *bytes);
+hstu_status hstu_layer_forward(const hstu_layer_args *args, hipStream_t stream);
+
+/* ======================================================================== */
+/* Instrumentation: kernel durations measured with HIP events               */
+/* ======================================================================== */
+
+/* When enabled (non-zero), every kernel the library launches is bracketed
+ * by a pair of HIP events recorded on the stream it is launched on.  Kernel
+ * names: "layer_norm", "f1_gemm", "append", "attention", "reduce_gate",
+ * "f2_gemm", "gather".  Enabling or disabling clears the records. */
+hstu_status hstu_timing_enable(int32_t enable);
+/* Waits for the recorded events of `kernel` and returns the number of
+ * launches and their summed duration in milliseconds; clears them.
+ * INVALID for an unknown name. */
+hstu_status hstu_timing_read(const char *kernel, int32_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSTU_H */

@@ -65,6 +65,8 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     f64p = ctypes.POINTER(ctypes.c_double)
     f32p = ctypes.POINTER(ctypes.c_float)
     vp = ctypes.c_void_p
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_layer_norm.restype = None
@@ -119,6 +121,11 @@ def offsets(lengths: Sequence[int]) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # elementwise pieces
 # ---------------------------------------------------------------------------
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return load(0).oracle_threads()
+
 
 def silu(z: float, mutant: int = 0) -> float:
     return load(mutant).oracle_silu(float(z))

@@ -35,6 +35,7 @@
  * the tests that prove the pins catch such mistakes).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,6 +48,9 @@
 #define ERR_INVALID 1
 #define ERR_NO_SPACE 2
 #define ERR_UNKNOWN_USER 3
+
+/* threads an OpenMP region of the oracle uses */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* elementwise pieces                                                        */

@@ -1,0 +1,93 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, rejects bad arguments with the documented status, and schedules a
+request plan whose work covers exactly the unmasked (query, key) pairs.
+No device call is made here."""
+import numpy as np
+import pytest
+
+from generative_recommender_sequence_amd import hstu
+from generative_recommender_sequence_amd.hstu import (HSTU_BF16, HSTU_ERR_INVALID, HSTU_ERR_UNSUPPORTED,
+                                                      HstuError)
+
+
+def test_exports_every_declared_symbol():
+    L = hstu.lib()
+    syms = hstu.header_symbols()
+    assert len(syms) >= 20
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(hstu.SIGNATURES)
+    assert L.hstu_abi_version() == 1
+
+
+def _status(fn, *a, **k):
+    try:
+        fn(*a, **k)
+        return 0
+    except HstuError as e:
+        return e.status
+
+
+def test_cache_create_validation():
+    assert _status(hstu.kv_cache_create, 1, 2, 128, 0, 10, HSTU_BF16) == HSTU_ERR_INVALID
+    assert _status(hstu.kv_cache_create, 1, 2, 128, 32, 3, HSTU_BF16, 0, 0, [0, 0, 1]) == HSTU_ERR_INVALID
+    assert _status(hstu.kv_cache_create, 1, 2, 12, 32, 3, HSTU_BF16) == HSTU_ERR_UNSUPPORTED
+    h = hstu.kv_cache_create(2, 2, 128, 32, 3, HSTU_BF16, 0, 0, [2, 0, 1])
+    assert hstu.kv_free_pages(h) == 3
+    assert "" == hstu.lib().hstu_last_error().decode()
+    # metadata-only cache cannot move data
+    assert _status(hstu.kv_page_append, h, 0, 1, 0, 0, 0, 1, 0, 0, 256, 1, 0) == HSTU_ERR_INVALID
+    assert b"without pools" in hstu.lib().hstu_last_error()
+    hstu.kv_cache_destroy(h)
+
+
+def test_plan_validation():
+    assert _status(hstu.hstu_plan_create, 2, 48, [3], [0], [0]) == HSTU_ERR_UNSUPPORTED
+    assert _status(hstu.hstu_plan_create, 2, 128, [3], [0], [4]) == HSTU_ERR_INVALID
+    assert _status(hstu.hstu_plan_create, 2, 128, [3], [-1], [0]) == HSTU_ERR_INVALID
+    assert _status(hstu.hstu_plan_create, 2, 128, [3], [0], [0], [0.0]) == HSTU_ERR_INVALID
+    p = hstu.hstu_plan_create(2, 128, [0, 3], [5, 0], [0, 0], [0.0, 3.0])   # n unused without new tokens
+    hstu.hstu_plan_destroy(p)
+    assert _status(hstu.hstu_plan_create, 2, 128, [70000], [0], [0]) == HSTU_ERR_UNSUPPORTED
+    assert _status(hstu.hstu_plan_create, 2, 128, [100], [0], [0], None, 32, 3) == HSTU_ERR_INVALID
+    p = hstu.hstu_plan_create(2, 128, [], [], [])
+    assert hstu.hstu_plan_get_info(p).n_new_total == 0
+    hstu.hstu_plan_destroy(p)
+
+
+def _visible_pairs(new_len, cached_len, n_targets):
+    tot = 0
+    for t, c, T in zip(new_len, cached_len, n_targets):
+        L = t + c
+        for i in range(c, L):
+            tot += i + 1 if i < L - T else L - T + 1
+    return tot
+
+
+@pytest.mark.parametrize("case", [
+    ([37, 64], [0, 0], [0, 0]),                       # small causal
+    ([300, 64, 1, 130], [0, 900, 0, 5000], [64, 64, 0, 130]),   # mixed hit/miss
+    ([256] * 40, [3000] * 40, [256] * 40),            # many cached users
+])
+def test_plan_counts_pairs_and_slots(case):
+    new_len, cached_len, n_targets = case
+    p = hstu.hstu_plan_create(4, 128, new_len, cached_len, n_targets, None, 32, 4096)
+    info = hstu.hstu_plan_get_info(p)
+    assert info.n_new_total == sum(new_len)
+    assert info.pairs == _visible_pairs(new_len, cached_len, n_targets)
+    n_qblocks = sum((t + 127) // 128 for t in new_len)
+    assert info.n_partial_slots >= n_qblocks * 4
+    assert info.n_work_items == info.n_partial_slots
+    assert info.attn_workspace_bytes >= info.n_partial_slots * 128 * 128 * 4
+    assert info.meta_bytes % 256 == 0
+    hstu.hstu_plan_destroy(p)
+
+
+def test_plan_rejects_use_before_upload():
+    p = hstu.hstu_plan_create(2, 128, [4], [0], [0])
+    args = hstu.hstu_attn_args()
+    args.dtype = HSTU_BF16
+    args.plan = p
+    assert _status(hstu.hstu_attn_fwd, args, 0) == HSTU_ERR_INVALID
+    assert b"not uploaded" in hstu.lib().hstu_last_error()
+    hstu.hstu_plan_destroy(p)

@@ -57,8 +57,30 @@ def test_model_vs_oracle_allocator(seed):
     _run_sequence(seed)
 
 
+@pytest.mark.parametrize("seed", range(40, 100))
+def test_library_vs_model_vs_oracle(seed):
+    _run_sequence(seed, with_lib=True)
+
+
+def test_library_dump_load_roundtrip():
+    from generative_recommender_sequence_amd import hstu
+    c = hstu.KVCache.host_only(12, 4, list(range(11, -1, -1)))
+    assert c.alloc([5, 9], [9, 2], 8)[0] == OK
+    snap = c.dump()
+    assert c.alloc([7], [13], 8)[0] == OK
+    assert c.evict_lru(8, [7])[0] == OK
+    assert c.dump() != snap
+    c.load(snap)
+    assert c.dump() == snap
+    bad = bytearray(snap)
+    bad[-4:] = bad[-8:-4]                      # a page listed twice
+    with pytest.raises(hstu.HstuError):
+        c.load(bytes(bad))
+    assert c.dump() == snap                    # unchanged after a failed load
+
+
 def test_exhaustion_and_all_pinned():
-    for impl in _impls(5, 4, [4, 3, 2, 1, 0]).values():
+    for impl in _impls(5, 4, [4, 3, 2, 1, 0], with_lib=True).values():
         rc, table, lens = impl.alloc([1, 2], [8, 8], 4)          # 2 + 2 pages
         assert rc == OK and [list(r[:2]) for r in table] == [[4, 3], [2, 1]]
         before = impl.dump()
@@ -80,7 +102,7 @@ def test_exhaustion_and_all_pinned():
 
 
 def test_lru_order_and_tie_break():
-    for impl in _impls(8, 1, None).values():
+    for impl in _impls(8, 1, None, with_lib=True).values():
         assert impl.alloc([30, 10, 20], [2, 2, 2], 8)[0] == OK
         assert impl.lookup([30])[0] == OK                         # 30 becomes most recent
         rc, ev = impl.evict_lru(6, [])
