@@ -16,14 +16,17 @@
 //
 // bf16 kernel (gfx950, 256 threads = 4 waves, 32 queries per wave):
 //   S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M rows, queries
-//   the N columns), so after SiLU each lane already holds, for its own query,
-//   the 8 key weights that form one A operand of O += P . V.  V is staged in
-//   LDS transposed ([dh][key]) with the key order permuted inside each
-//   16-key group (bits 2 and 3 swapped) so a B operand is one 16-byte read;
-//   rows are XOR-swizzled by 16-byte chunk to keep both the transposing
-//   writes and the reads free of bank conflicts.  The bias of a tile comes
-//   from a reversed per-tile table in LDS read with immediate offsets, or from
-//   one scalar when a wave's whole distance range falls in a single bucket.
+//   the N columns).  MFMA row i of a 32-key block reads key i with bits 2 and
+//   3 swapped, so after SiLU each lane holds, for its own query, 8 consecutive
+//   key weights per 16-key step: exactly one A operand of O += P . V.
+//   K and V tiles are staged row-major in LDS (16-byte-chunk XOR swizzles);
+//   the V operand is read with ds_read_b64_tr_b16, which hands each lane 4
+//   consecutive keys of one column, so V is never transposed in registers.
+//   The next tile's K/V rows are fetched into registers while the current
+//   tile is multiplied, and the work item's page-table slice is staged in LDS
+//   once, so no tile waits on a dependent page-table load.  The bias of a tile
+//   comes from a reversed per-tile table in LDS read with immediate offsets,
+//   or from one scalar when a wave's distance range falls in a single bucket.
 //   Masking work is only done on tiles that touch the diagonal or the
 //   candidate block.
 #include "common.h"
@@ -45,33 +48,31 @@ __device__ __forceinline__ float rab_at(const float* rab, int nb, int delta) {
   return delta < 0 ? 0.f : rab[rel_bucket(delta, nb)];
 }
 
-// position inside a 16-key group of LDS V^T: swap key bits 2 and 3
+// Key order inside each 32-key MFMA row block: MFMA row i reads key vperm(i)
+// (bits 2 and 3 swapped), so that after S^T = K . Q^T the 8 score registers a
+// lane feeds into one P . V k-step are 8 consecutive keys.
 __device__ __forceinline__ int vperm(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
-__device__ __forceinline__ int vswz(int d, int chunk) { return chunk ^ ((d + (d >> 3)) & 7); }
+// 16-byte-chunk XOR swizzles of the K and V tiles ([64 keys][128 dims] each)
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+__device__ __forceinline__ int vswz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 
-template <bool PAGED>
-__device__ __forceinline__ const uint16_t* kv_row(const AttnLaunch& a, const uint16_t* base,
-                                                  const UserInfo& ui, int user, int h, int j) {
-  if (PAGED) {
-    const int P = a.plan.page_size;
-    int lp = j / P;
-    if (lp >= a.plan.max_pages) return nullptr;
-    int page = a.page_table[static_cast<int64_t>(user) * a.plan.max_pages + lp];
-    if (page < 0 || page >= a.num_pages) return nullptr;
-    return base + a.pool_layer_offset +
-           ((static_cast<int64_t>(page) * a.plan.H + h) * P + (j % P)) * DH;
-  } else {
-    return base + static_cast<int64_t>(ui.kv_row0 + j) * a.kv_stride + h * DH;
-  }
+constexpr int kMaxPagesLds = 2048;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * DH];
   __shared__ float bias_rev[256];
+  __shared__ int32_t pages_lds[PAGED ? kMaxPagesLds : 1];
 
   const WorkItem w = a.plan.items[blockIdx.x];
   const QBlock qb = a.plan.qblocks[w.qblock];
@@ -90,6 +91,37 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(PAGED ? a.k_pool : a.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(PAGED ? a.v_pool : a.v);
 
+  // ---- this work item's slice of the page table, staged once ----
+  const int P = PAGED ? a.plan.page_size : 1;
+  const bool p_pow2 = (P & (P - 1)) == 0;
+  const int p_shift = p_pow2 ? __ffs(P) - 1 : 0;
+  int pg0 = 0;
+  bool pt_lds = false;
+  if (PAGED) {
+    pg0 = (w.tile_begin * KT) / P;
+    int pg1 = min((w.tile_end * KT + P - 1) / P, a.plan.max_pages);
+    int npg = pg1 - pg0;
+    pt_lds = npg <= kMaxPagesLds;
+    if (pt_lds) {
+      const int32_t* src = a.page_table + static_cast<int64_t>(w.user) * a.plan.max_pages + pg0;
+      for (int i = tid; i < npg; i += 256) pages_lds[i] = src[i];
+    }
+  }
+  // element offset of key position j's row for this head, or -1
+  auto row_off = [&](int j) -> int64_t {
+    if (j >= ui.kv_len) return -1;
+    if (PAGED) {
+      int lp = p_pow2 ? (j >> p_shift) : (j / P);
+      int slot = p_pow2 ? (j & (P - 1)) : (j - lp * P);
+      int page;
+      if (pt_lds) page = pages_lds[lp - pg0];
+      else page = lp < a.plan.max_pages ? a.page_table[static_cast<int64_t>(w.user) * a.plan.max_pages + lp] : -1;
+      if (page < 0 || page >= a.num_pages) return -1;
+      return a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + slot) * DH;
+    }
+    return static_cast<int64_t>(ui.kv_row0 + j) * a.kv_stride + h * DH;
+  };
+
   // Q^T as the B operand of S^T = K . Q^T: lane holds q[query l32][16 s + 8 g .. +8]
   bf16x8 qf[DH / 16];
   {
@@ -106,80 +138,96 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
   for (int t = 0; t < DH / 32; ++t) oacc[t] = f32x16{};
 
-  // loader roles: K rows key = tid/16 + 16 i, 16-byte chunk tid%16;
-  // V: chunk dc = tid%16 (dims 8dc..8dc+7), keys 4*(tid/16) .. +3
+  // loader role: rows lr + 16 i (i < 4), 16-byte chunk lc
   const int lc = tid & 15, lr = tid >> 4;
+  u32x4 kreg[4], vreg[4];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t off = row_off(tile * KT + lr + 16 * i);
+      kreg[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(kbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(vbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
-  for (int tile = w.tile_begin; tile < w.tile_end; ++tile) {
-    const int k0 = tile * KT;
-    if (!tile_visible_dev(k0, qa, qe, hist)) continue;  // uniform over the block
-    __syncthreads();  // previous tile's LDS reads are done
-    // ---- stage K (row-major) and V^T (permuted, swizzled) ----
+  // per-lane LDS read addresses (elements), hoisted out of the tile loop
+  int kaddr[DH / 16];  // A operand of S^T: row vperm(l32) (+32 per row block), chunk (2s+g)
+  {
+    const int row = vperm(l32);
 #pragma unroll
-    for (int i = 0; i < KT / 16; ++i) {
-      int key = lr + 16 * i;
-      int j = k0 + key;
-      const uint16_t* src = j < ui.kv_len ? kv_row<PAGED>(a, kbase, ui, w.user, h, j) : nullptr;
-      u32x4 v = src ? *reinterpret_cast<const u32x4*>(src + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&Ks[key * DH + 8 * (lc ^ (key & 7))]) = v;
-    }
-    {
-      u32x4 vr[4];
+    for (int s = 0; s < DH / 16; ++s) kaddr[s] = row * DH + 8 * ((2 * s + g) ^ kswz(row));
+  }
+  int vaddr[2][DH / 32];  // transposed B-operand reads of V: keys 4r + j/4 (+8g, +16ks), dims 32nt + ...
+  {
+    const int grp = lane >> 4, j = lane & 15;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        int j = k0 + 4 * lr + m;
-        const uint16_t* src = j < ui.kv_len ? kv_row<PAGED>(a, vbase, ui, w.user, h, j) : nullptr;
-        vr[m] = src ? *reinterpret_cast<const u32x4*>(src + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-      }
-      const int pos = vperm(4 * lr);  // 4 consecutive keys stay consecutive
+    for (int r = 0; r < 2; ++r) {
+      const int row = 8 * g + 4 * r + (j >> 2);  // plus 16 ks (does not change the swizzle)
+      const int dcol = 16 * (grp & 1) + 4 * (j & 3);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int d = 8 * lc + e;
-        uint32_t w0 = (e & 1) ? (vr[0][e >> 1] >> 16) : (vr[0][e >> 1] & 0xFFFFu);
-        uint32_t w1 = (e & 1) ? (vr[1][e >> 1] >> 16) : (vr[1][e >> 1] & 0xFFFFu);
-        uint32_t w2 = (e & 1) ? (vr[2][e >> 1] >> 16) : (vr[2][e >> 1] & 0xFFFFu);
-        uint32_t w3 = (e & 1) ? (vr[3][e >> 1] >> 16) : (vr[3][e >> 1] & 0xFFFFu);
-        u32x2 pk = {w0 | (w1 << 16), w2 | (w3 << 16)};
-        int chunk = vswz(d, pos >> 3);
-        *reinterpret_cast<u32x2*>(&Vt[d * KT + 8 * chunk + (pos & 7)]) = pk;
+      for (int nt = 0; nt < DH / 32; ++nt) {
+        int d = 32 * nt + dcol;
+        vaddr[r][nt] = row * DH + 8 * ((d >> 3) ^ vswz(row)) + (d & 7);
       }
     }
-    // ---- reversed bias table: bias_rev[t] = rab(b(delta_hi - t)) ----
+  }
+
+  auto visible_tile = [&](int t) { return tile_visible_dev(t * KT, qa, qe, hist); };
+  int t = w.tile_begin;
+  while (t < w.tile_end && !visible_tile(t)) ++t;
+  __syncthreads();  // page table slice staged
+  if (t < w.tile_end) fetch(t);
+
+  while (t < w.tile_end) {
+    int tn = t + 1;
+    while (tn < w.tile_end && !visible_tile(tn)) ++tn;
+    const int k0 = t * KT;
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = lr + 16 * i;
+      *reinterpret_cast<u32x4*>(&Ks[row * DH + 8 * (lc ^ kswz(row))]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[row * DH + 8 * (lc ^ vswz(row))]) = vreg[i];
+    }
+    // reversed bias table of this tile: bias_rev[i] = rab(b(delta_hi - i))
     const int delta_hi = qa + BQ - 1 - k0;
     if (tid < kBiasLen) bias_rev[tid] = rab_at(a.rab, nb, delta_hi - tid);
     __syncthreads();
-    if (!wave_active) continue;
+    if (tn < w.tile_end) fetch(tn);  // in flight while this tile is computed
+    if (!wave_active) {
+      t = tn;
+      continue;
+    }
 
-    // ---- S^T = K . Q^T ----
+    // ---- S^T = K . Q^T (register r of block mt: key 32 mt + 16 (r/8) + 8 g + r%8) ----
     f32x16 sacc[KT / 32];
 #pragma unroll
     for (int mt = 0; mt < KT / 32; ++mt) {
       sacc[mt] = f32x16{};
-      int key = 32 * mt + l32;
 #pragma unroll
       for (int s = 0; s < DH / 16; ++s) {
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[key * DH + 8 * ((2 * s + g) ^ (key & 7))]);
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[kaddr[s] + 32 * mt * DH]);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[mt], 0, 0, 0);
       }
     }
 
     // ---- bias, mask, SiLU ----
-    // lane's keys: k0 + 32 mt + 8 (r/4) + 4 g + (r%4); distance qpos - key
     const int wq_lo = qa + wq0, wq_hi = qa + wq0 + 31;
     const int dmin = wq_lo - (k0 + KT - 1), dmax = wq_hi - k0;
     const bool full = (k0 + KT - 1 < wq_lo) && (k0 + KT - 1 < hist);  // no masking needed
     const bool uni = dmin >= 0 && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
     const float ubias = uni ? a.rab[rel_bucket(dmax, nb)] : 0.f;
-    const float* brow = &bias_rev[BQ - 1 - qlocal + 4 * g];  // + 32 mt + 8 (r/4) + r%4
+    const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
+    const int kbase_lane = k0 + 8 * g;
 #pragma unroll
     for (int mt = 0; mt < KT / 32; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int koff = 32 * mt + 8 * (r >> 2) + (r & 3);
+        const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
         float x = sacc[mt][r] + (uni ? ubias : brow[koff]);
         float p = silu_fast(x);
         if (!full) {
-          const int key = k0 + koff + 4 * g;
+          const int key = kbase_lane + koff;
           const bool vis = (key == qpos) || (key < qpos && key < hist);
           p = vis ? p : 0.f;
         }
@@ -187,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch a) {
       }
     }
 
-    // ---- O += P . V ----
+    // ---- O += P . V (V read transposed from its row-major tile) ----
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
       const f32x16& src = sacc[ks >> 1];
@@ -197,11 +245,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch a) {
       for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(src[base + e]);
 #pragma unroll
       for (int nt = 0; nt < DH / 32; ++nt) {
-        int d = 32 * nt + l32;
-        bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vt[d * KT + 8 * vswz(d, 2 * ks + g)]);
+        // assembled from whole dwords: extracting the 16-bit elements of the
+        // transposed reads one by one is lowered incorrectly by this compiler
+        u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&Vs[vaddr[0][nt] + 16 * ks * DH]));
+        u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&Vs[vaddr[1][nt] + 16 * ks * DH]));
+        bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
         oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[nt], 0, 0, 0);
       }
     }
+    t = tn;
   }
 
   if (!wave_active) return;
