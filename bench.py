@@ -63,7 +63,19 @@ def main(argv=None):
     ap.add_argument("--workload", default="C4", choices=["C2", "C3", "C4", "C5"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (reference for HBM traffic counters)")
     args = ap.parse_args(argv)
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}), flush=True)
         sys.exit(2)

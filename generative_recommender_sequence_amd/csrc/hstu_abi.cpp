@@ -47,6 +47,8 @@ size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
 // small that their partial tile costs more than the keys they read.
 constexpr int kTargetPieces = 1024;
 constexpr int kMinPieceTiles = 4;
+constexpr int kMaxPieceTiles = 256;  // bounds a work item's staged page-table slice
+constexpr int kXcds = 8;             // workgroups are dealt to the 8 XCDs round-robin
 
 bool tile_visible(int64_t k0, int64_t qa, int64_t qe, int64_t hist) {
   // some key j in [k0, k0+kTileK) visible to some query i in [qa, qe):
@@ -159,8 +161,8 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
       if (tile_visible(static_cast<int64_t>(t) * kTileK, qa, qe, ui.hist)) vis[b].push_back(t);
     total += static_cast<int64_t>(vis[b].size()) * H;
   }
-  int64_t piece_tiles =
-      std::max<int64_t>(kMinPieceTiles, (total + kTargetPieces - 1) / kTargetPieces);
+  int64_t piece_tiles = std::min<int64_t>(
+      kMaxPieceTiles, std::max<int64_t>(kMinPieceTiles, (total + kTargetPieces - 1) / kTargetPieces));
   p->qb_slots.resize(static_cast<size_t>(nqb) * H);
   std::vector<std::pair<int32_t, WorkItem>> pieces;  // (visible tiles, item)
   int32_t slot = 0;
@@ -185,9 +187,47 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     }
   }
   p->n_slots = slot;
-  std::stable_sort(pieces.begin(), pieces.end(),
-                   [](const auto& a, const auto& b) { return a.first > b.first; });
-  for (const auto& pc : pieces) p->items.push_back(pc.second);
+  // Dispatch order.  Pieces of one (user, head) read the same K/V, so they
+  // go to one XCD and run there together, sharing its L2.  Groups are dealt
+  // to XCDs largest first onto the least-loaded one; inside an XCD, groups
+  // and pieces run longest first.  Block b runs on XCD b % 8, so XCD x's
+  // k-th piece sits at index 8k + x; short queues are padded with no-op
+  // entries (slot -1).
+  {
+    std::vector<std::vector<std::pair<int32_t, WorkItem>>> groups;
+    std::vector<int64_t> gcost;
+    std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1);
+    for (const auto& pc : pieces) {
+      int32_t key = pc.second.user * H + pc.second.head;
+      if (gid[key] < 0) {
+        gid[key] = static_cast<int32_t>(groups.size());
+        groups.emplace_back();
+        gcost.push_back(0);
+      }
+      groups[gid[key]].push_back(pc);
+      gcost[gid[key]] += pc.first;
+    }
+    std::vector<int32_t> gorder(groups.size());
+    std::iota(gorder.begin(), gorder.end(), 0);
+    std::stable_sort(gorder.begin(), gorder.end(),
+                     [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+    std::vector<std::vector<WorkItem>> q(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    for (int32_t gi : gorder) {
+      int x = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      auto& grp = groups[gi];
+      std::stable_sort(grp.begin(), grp.end(),
+                       [](const auto& a, const auto& b) { return a.first > b.first; });
+      for (const auto& pc : grp) q[x].push_back(pc.second);
+      load[x] += gcost[gi];
+    }
+    size_t depth = 0;
+    for (const auto& qq : q) depth = std::max(depth, qq.size());
+    WorkItem pad{};
+    pad.slot = -1;
+    for (size_t k = 0; k < depth; ++k)
+      for (int x = 0; x < kXcds; ++x) p->items.push_back(k < q[x].size() ? q[x][k] : pad);
+  }
 
   // packed device image
   auto& blob = p->host_blob;
@@ -340,6 +380,9 @@ static hstu_status fill_keys(AttnLaunch& L, const hstu_plan* p, int dtype, const
       return fail(HSTU_ERR_INVALID, std::string(who) + ": cache geometry differs from the plan");
     if (layer < 0 || layer >= cache->num_layers)
       return fail(HSTU_ERR_INVALID, std::string(who) + ": bad layer");
+    const int P = cache->page_size;
+    if (dtype == HSTU_BF16 && (P < 16 || (P & (P - 1)) != 0))
+      return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": bf16 pages must hold a power of two >= 16 tokens");
     L.k_pool = cache->k_pool;
     L.v_pool = cache->v_pool;
     L.pool_layer_offset =
@@ -367,6 +410,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   if (p->n_new == 0) return ok();
   if (!a->q || !a->out || !a->rab || a->num_buckets <= 0)
     return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null q/out/rab or no buckets");
+  if (a->num_buckets > 256) return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_fwd: more than 256 buckets");
   if (a->q_row_stride < static_cast<int64_t>(H) * dh || a->q_row_stride % 8)
     return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: bad q_row_stride");
   hstu_plan_info info{};
@@ -432,6 +476,7 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   if (p->n_new == 0) return ok();
   if (!a->x || !a->y || !a->w1 || !a->w2 || !a->rab || a->num_buckets <= 0)
     return fail(HSTU_ERR_INVALID, "hstu_layer_forward: null x/y/w1/w2/rab or no buckets");
+  if (a->num_buckets > 256) return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_forward: more than 256 buckets");
   const size_t xbytes = static_cast<size_t>(p->n_new) * d * esize(a->dtype);
   {
     auto xb = reinterpret_cast<uintptr_t>(a->x), yb = reinterpret_cast<uintptr_t>(a->y);

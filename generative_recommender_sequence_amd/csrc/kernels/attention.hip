@@ -44,21 +44,21 @@ __device__ __forceinline__ bool tile_visible_dev(int k0, int qa, int qe, int his
   return k0 < hist && k0 < qe - 1;
 }
 
-__device__ __forceinline__ float rab_at(const float* rab, int nb, int delta) {
-  return delta < 0 ? 0.f : rab[rel_bucket(delta, nb)];
-}
-
 // Key order inside each 32-key MFMA row block: MFMA row i reads key vperm(i)
 // (bits 2 and 3 swapped), so that after S^T = K . Q^T the 8 score registers a
 // lane feeds into one P . V k-step are 8 consecutive keys.
 __device__ __forceinline__ int vperm(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
-// 16-byte-chunk XOR swizzles of the K and V tiles ([64 keys][128 dims] each)
+// 16-byte-chunk XOR swizzles of the K and V tiles ([64 keys][128 dims] each).
+// K: the 16 rows an A-operand read touches per cycle map to 16 chunk slots.
+// V: the 4 rows x 2 chunks a 16-lane transposed read touches (and the other
+// half-wave's 2 chunks) map to distinct slots.
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int vswz(int row) { return (row & 3) << 2; }
 
 constexpr int kMaxPagesLds = 2048;
+constexpr int kMaxBuckets = 256;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -67,14 +67,18 @@ __device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <bool PAGED>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * DH];
   __shared__ float bias_rev[256];
+  __shared__ float rab_s[kMaxBuckets];
   __shared__ int32_t pages_lds[PAGED ? kMaxPagesLds : 1];
 
   const WorkItem w = a.plan.items[blockIdx.x];
+  if (w.slot < 0) return;  // padding entry of the dispatch order
   const QBlock qb = a.plan.qblocks[w.qblock];
   const UserInfo ui = a.plan.users[w.user];
   const int h = w.head;
@@ -91,36 +95,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(PAGED ? a.k_pool : a.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(PAGED ? a.v_pool : a.v);
 
-  // ---- this work item's slice of the page table, staged once ----
+  // ---- stage the bias table and this work item's page-table slice ----
+  for (int i = tid; i < nb; i += 256) rab_s[i] = a.rab[i];
   const int P = PAGED ? a.plan.page_size : 1;
-  const bool p_pow2 = (P & (P - 1)) == 0;
-  const int p_shift = p_pow2 ? __ffs(P) - 1 : 0;
-  int pg0 = 0;
-  bool pt_lds = false;
+  const int p_shift = __ffs(P) - 1;          // the host guarantees a power of two
+  int pg0 = 0, npg = 0;
   if (PAGED) {
-    pg0 = (w.tile_begin * KT) / P;
-    int pg1 = min((w.tile_end * KT + P - 1) / P, a.plan.max_pages);
-    int npg = pg1 - pg0;
-    pt_lds = npg <= kMaxPagesLds;
-    if (pt_lds) {
-      const int32_t* src = a.page_table + static_cast<int64_t>(w.user) * a.plan.max_pages + pg0;
-      for (int i = tid; i < npg; i += 256) pages_lds[i] = src[i];
-    }
+    pg0 = (w.tile_begin * KT) >> p_shift;
+    int pg1 = min((w.tile_end * KT + P - 1) >> p_shift, a.plan.max_pages);
+    npg = pg1 - pg0;
+    const int32_t* src = a.page_table + static_cast<int64_t>(w.user) * a.plan.max_pages + pg0;
+    for (int i = tid; i < npg; i += 256) pages_lds[i] = src[i];
   }
-  // element offset of key position j's row for this head, or -1
-  auto row_off = [&](int j) -> int64_t {
-    if (j >= ui.kv_len) return -1;
-    if (PAGED) {
-      int lp = p_pow2 ? (j >> p_shift) : (j / P);
-      int slot = p_pow2 ? (j & (P - 1)) : (j - lp * P);
-      int page;
-      if (pt_lds) page = pages_lds[lp - pg0];
-      else page = lp < a.plan.max_pages ? a.page_table[static_cast<int64_t>(w.user) * a.plan.max_pages + lp] : -1;
-      if (page < 0 || page >= a.num_pages) return -1;
-      return a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + slot) * DH;
-    }
-    return static_cast<int64_t>(ui.kv_row0 + j) * a.kv_stride + h * DH;
-  };
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds q[query l32][16 s + 8 g .. +8]
   bf16x8 qf[DH / 16];
@@ -138,15 +124,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
   for (int t = 0; t < DH / 32; ++t) oacc[t] = f32x16{};
 
-  // loader role: rows lr + 16 i (i < 4), 16-byte chunk lc
+  // ---- loader: rows lr + 16 i (i < 4) of a tile, 16-byte chunk lc ----
+  // Every 16-row group of a wave lies in one page for page sizes >= 16, so the
+  // page of row i is wave-uniform and its address math is scalar.
   const int lc = tid & 15, lr = tid >> 4;
   u32x4 kreg[4], vreg[4];
   auto fetch = [&](int tile) {
+    const int k0 = tile * KT;
+    const bool tail = k0 + KT > ui.kv_len;  // uniform
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int64_t off = row_off(tile * KT + lr + 16 * i);
-      kreg[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(kbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = off >= 0 ? *reinterpret_cast<const u32x4*>(vbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+      const int r = lr + 16 * i;
+      int64_t off;
+      bool ok = !tail || (k0 + r < ui.kv_len);
+      if (PAGED) {
+        const int j = k0 + r;
+        const int lp = j >> p_shift;
+        int page = pages_lds[lp - pg0];
+        if (P >= 16) page = uniform(page);
+        ok = ok && page >= 0 && page < a.num_pages;
+        off = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (j & (P - 1))) * DH;
+      } else {
+        off = static_cast<int64_t>(ui.kv_row0 + k0 + r) * a.kv_stride + h * DH;
+      }
+      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(kbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(vbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) kaddr[s] = row * DH + 8 * ((2 * s + g) ^ kswz(row));
   }
-  int vaddr[2][DH / 32];  // transposed B-operand reads of V: keys 4r + j/4 (+8g, +16ks), dims 32nt + ...
+  int vaddr[2][DH / 32];  // transposed B-operand reads of V
   {
     const int grp = lane >> 4, j = lane & 15;
 #pragma unroll
@@ -175,13 +177,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   auto visible_tile = [&](int t) { return tile_visible_dev(t * KT, qa, qe, hist); };
   int t = w.tile_begin;
   while (t < w.tile_end && !visible_tile(t)) ++t;
-  __syncthreads();  // page table slice staged
+  __syncthreads();  // rab and page-table slice staged
   if (t < w.tile_end) fetch(t);
 
   while (t < w.tile_end) {
     int tn = t + 1;
     while (tn < w.tile_end && !visible_tile(tn)) ++tn;
     const int k0 = t * KT;
+    // distances this block's queries see in this tile; one bucket -> no table
+    const int blk_dlo = qa - (k0 + KT - 1), blk_dhi = qe - 1 - k0;
+    const bool blk_uni = blk_dlo >= 0 && rel_bucket(blk_dlo, nb) == rel_bucket(blk_dhi, nb);
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -189,9 +194,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
       *reinterpret_cast<u32x4*>(&Ks[row * DH + 8 * (lc ^ kswz(row))]) = kreg[i];
       *reinterpret_cast<u32x4*>(&Vs[row * DH + 8 * (lc ^ vswz(row))]) = vreg[i];
     }
-    // reversed bias table of this tile: bias_rev[i] = rab(b(delta_hi - i))
-    const int delta_hi = qa + BQ - 1 - k0;
-    if (tid < kBiasLen) bias_rev[tid] = rab_at(a.rab, nb, delta_hi - tid);
+    if (!blk_uni && tid < kBiasLen) {
+      // reversed bias table of this tile: bias_rev[i] = rab(b(delta_hi - i))
+      const int d = qa + BQ - 1 - k0 - tid;
+      bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
+    }
     __syncthreads();
     if (tn < w.tile_end) fetch(tn);  // in flight while this tile is computed
     if (!wave_active) {
@@ -212,27 +219,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     }
 
     // ---- bias, mask, SiLU ----
-    const int wq_lo = qa + wq0, wq_hi = qa + wq0 + 31;
+    const int wq_lo = qa + wq0, wq_hi = min(qa + wq0 + 31, qe - 1);
     const int dmin = wq_lo - (k0 + KT - 1), dmax = wq_hi - k0;
     const bool full = (k0 + KT - 1 < wq_lo) && (k0 + KT - 1 < hist);  // no masking needed
     const bool uni = dmin >= 0 && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
-    const float ubias = uni ? a.rab[rel_bucket(dmax, nb)] : 0.f;
-    const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
     const int kbase_lane = k0 + 8 * g;
+    if (uni) {
+      const float ub = rab_s[rel_bucket(dmax, nb)];
 #pragma unroll
-    for (int mt = 0; mt < KT / 32; ++mt) {
+      for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
-        float x = sacc[mt][r] + (uni ? ubias : brow[koff]);
-        float p = silu_fast(x);
-        if (!full) {
-          const int key = kbase_lane + koff;
-          const bool vis = (key == qpos) || (key < qpos && key < hist);
-          p = vis ? p : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = silu_fast(sacc[mt][r] + ub);
+          if (!full) {
+            const int key = kbase_lane + 32 * mt + 16 * (r >> 3) + (r & 7);
+            p = ((key == qpos) || (key < qpos && key < hist)) ? p : 0.f;
+          }
+          sacc[mt][r] = p;
         }
-        sacc[mt][r] = p;
-      }
+    } else {
+      const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
+#pragma unroll
+      for (int mt = 0; mt < KT / 32; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
+          float p = silu_fast(sacc[mt][r] + brow[koff]);
+          const int key = kbase_lane + koff;
+          p = ((key == qpos) || (key < qpos && key < hist)) ? p : 0.f;
+          sacc[mt][r] = p;
+        }
     }
 
     // ---- O += P . V (V read transposed from its row-major tile) ----
@@ -277,6 +293,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
   __shared__ float Ks[SK][D + 1];
   __shared__ float Vs[SK][D + 1];
   const WorkItem w = a.plan.items[blockIdx.x];
+  if (w.slot < 0) return;  // padding entry of the dispatch order
   const QBlock qb = a.plan.qblocks[w.qblock];
   const UserInfo ui = a.plan.users[w.user];
   const int h = w.head, tid = threadIdx.x;

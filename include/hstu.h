@@ -183,7 +183,8 @@ typedef struct {
 
 typedef struct {
   int32_t n_new_total;       /* sum t_u */
-  int32_t n_work_items;      /* attention work items (query block x head x key range) */
+  int32_t n_work_items;      /* attention blocks launched: work items (query block x head x key
+                              * range) plus no-op padding of the XCD-aware order */
   int32_t n_partial_slots;   /* fp32 [128][head_dim] partial tiles */
   int64_t pairs;             /* unmasked (query, key) pairs per head */
   size_t meta_bytes;         /* device bytes hstu_plan_upload needs */

@@ -77,7 +77,7 @@ def test_plan_counts_pairs_and_slots(case):
     assert info.pairs == _visible_pairs(new_len, cached_len, n_targets)
     n_qblocks = sum((t + 127) // 128 for t in new_len)
     assert info.n_partial_slots >= n_qblocks * 4
-    assert info.n_work_items == info.n_partial_slots
+    assert info.n_work_items >= info.n_partial_slots and info.n_work_items % 8 == 0
     assert info.attn_workspace_bytes >= info.n_partial_slots * 128 * 128 * 4
     assert info.meta_bytes % 256 == 0
     hstu.hstu_plan_destroy(p)
