@@ -430,7 +430,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
     return st;
   if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_attn_fwd: attention")) != HSTU_OK)
     return st;
-  return check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, nullptr, 0, 0.f, a->out,
+  return check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, partial_scale(a->dtype), nullptr, 0, 0.f, a->out,
                                       nullptr, stream); }),
                    "hstu_attn_fwd: reduce");
 }
@@ -536,7 +536,7 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   }
   if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_layer_forward: attention")) != HSTU_OK)
     return st;
-  if ((st = check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, partials, uvqk, 4 * inner, a->eps,
+  if ((st = check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, partials, partial_scale(a->dtype), uvqk, 4 * inner, a->eps,
                                          a->o_out, g, stream); }),
                       "hstu_layer_forward: LayerNorm gate")) != HSTU_OK)
     return st;

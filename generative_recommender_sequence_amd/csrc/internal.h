@@ -149,11 +149,14 @@ struct AttnLaunch {
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
-// Sums each row's partial slots in key order, scales by 1/n_u; then either
+// Sums each row's partial slots in key order, scales by o_scale / n_u; then
 // writes o (fp32) and/or g = LayerNorm(o) * U (dtype).
 hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials,
-                              const void* u, int64_t u_stride, float eps, float* o_out,
-                              void* g_out, hipStream_t s);
+                              float o_scale, const void* u, int64_t u_stride, float eps,
+                              float* o_out, void* g_out, hipStream_t s);
+// The bf16 attention's partial sums carry a factor log2(e); this removes it.
+constexpr float kBf16PartialScale = 0.693147180559945309f;
+inline float partial_scale(int dtype) { return dtype == HSTU_BF16 ? kBf16PartialScale : 1.0f; }
 
 // y = LayerNorm(x) rows (no affine) -> xhat (dtype)
 hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows, int32_t cols,

@@ -69,12 +69,20 @@ __device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Weights carry a factor log2(e): with y = log2(e) * x, the kernel forms
+// y / (1 + 2^-y) = log2(e) * SiLU(x) (one FMA, one exp2, one add, one rcp,
+// one multiply); the reduction multiplies by ln 2 to remove it.
+constexpr float kLog2e = 1.44269504088896340736f;
+__device__ __forceinline__ float silu_l2(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y));
+}
+
 template <bool PAGED>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * DH];
-  __shared__ float bias_rev[256];
-  __shared__ float rab_s[kMaxBuckets];
+  __shared__ float bias_rev[256];     // log2(e) * bias, reversed distance order
+  __shared__ float rab_s[kMaxBuckets];  // log2(e) * rab
   __shared__ int32_t pages_lds[PAGED ? kMaxPagesLds : 1];
 
   const WorkItem w = a.plan.items[blockIdx.x];
@@ -82,7 +90,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   const QBlock qb = a.plan.qblocks[w.qblock];
   const UserInfo ui = a.plan.users[w.user];
   const int h = w.head;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = uniform(tid >> 6);
   const int wq0 = wave * 32;                 // first local query of this wave
   const bool wave_active = wq0 < qb.count;
   const int qlocal = wq0 + l32;
@@ -90,22 +99,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   const int qa = qb.pos0, qe = qb.pos0 + qb.count;
   const int hist = ui.hist;
   const int nb = a.num_buckets;
+  const int vis_lim = min(qpos, hist);       // keys below this are visible; so is key == qpos
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
   const uint16_t* kbase = static_cast<const uint16_t*>(PAGED ? a.k_pool : a.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(PAGED ? a.v_pool : a.v);
 
   // ---- stage the bias table and this work item's page-table slice ----
-  for (int i = tid; i < nb; i += 256) rab_s[i] = a.rab[i];
-  const int P = PAGED ? a.plan.page_size : 1;
+  for (int i = tid; i < nb; i += 256) rab_s[i] = a.rab[i] * kLog2e;
+  const int P = PAGED ? a.plan.page_size : KT;
   const int p_shift = __ffs(P) - 1;          // the host guarantees a power of two
-  int pg0 = 0, npg = 0;
+  int pg0 = 0;
   if (PAGED) {
     pg0 = (w.tile_begin * KT) >> p_shift;
     int pg1 = min((w.tile_end * KT + P - 1) >> p_shift, a.plan.max_pages);
-    npg = pg1 - pg0;
     const int32_t* src = a.page_table + static_cast<int64_t>(w.user) * a.plan.max_pages + pg0;
-    for (int i = tid; i < npg; i += 256) pages_lds[i] = src[i];
+    for (int i = tid; i < pg1 - pg0; i += 256) pages_lds[i] = src[i];
   }
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds q[query l32][16 s + 8 g .. +8]
@@ -125,30 +134,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   for (int t = 0; t < DH / 32; ++t) oacc[t] = f32x16{};
 
   // ---- loader: rows lr + 16 i (i < 4) of a tile, 16-byte chunk lc ----
-  // Every 16-row group of a wave lies in one page for page sizes >= 16, so the
-  // page of row i is wave-uniform and its address math is scalar.
+  // The 4 rows a wave loads per i are consecutive, so for pages of 16+
+  // tokens they share one page: the row-group base is scalar and each lane
+  // adds a constant offset.
   const int lc = tid & 15, lr = tid >> 4;
+  const int pm = P < KT ? P : KT;
+  int loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lr + 16 * i;
+    loff[i] = PAGED ? (r & (pm - 1)) * DH + 8 * lc
+                    : r * static_cast<int>(a.kv_stride) + h * DH + 8 * lc;
+  }
   u32x4 kreg[4], vreg[4];
   auto fetch = [&](int tile) {
     const int k0 = tile * KT;
-    const bool tail = k0 + KT > ui.kv_len;  // uniform
+    const bool tail = k0 + KT > ui.kv_len;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = lr + 16 * i;
-      int64_t off;
-      bool ok = !tail || (k0 + r < ui.kv_len);
+      int64_t base;
+      bool ok = !tail || (k0 + lr + 16 * i < ui.kv_len);
       if (PAGED) {
-        const int j = k0 + r;
-        const int lp = j >> p_shift;
-        int page = pages_lds[lp - pg0];
-        if (P >= 16) page = uniform(page);
+        const int lp = (k0 + 16 * i + 4 * wave) >> p_shift;
+        const int page = uniform(pages_lds[lp - pg0]);
         ok = ok && page >= 0 && page < a.num_pages;
-        off = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (j & (P - 1))) * DH;
+        base = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (k0 & (P - 1))) * DH;
       } else {
-        off = static_cast<int64_t>(ui.kv_row0 + k0 + r) * a.kv_stride + h * DH;
+        base = static_cast<int64_t>(ui.kv_row0 + k0) * a.kv_stride;
       }
-      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(kbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(vbase + off + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(kbase + base + loff[i]) : u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(vbase + base + loff[i]) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -195,7 +210,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
       *reinterpret_cast<u32x4*>(&Vs[row * DH + 8 * (lc ^ vswz(row))]) = vreg[i];
     }
     if (!blk_uni && tid < kBiasLen) {
-      // reversed bias table of this tile: bias_rev[i] = rab(b(delta_hi - i))
       const int d = qa + BQ - 1 - k0 - tid;
       bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
     }
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
       }
     }
 
-    // ---- bias, mask, SiLU ----
+    // ---- bias, mask, SiLU: weights y / (1 + 2^-y) with y = log2(e) (q.k + bias) ----
     const int wq_lo = qa + wq0, wq_hi = min(qa + wq0 + 31, qe - 1);
     const int dmin = wq_lo - (k0 + KT - 1), dmax = wq_hi - k0;
     const bool full = (k0 + KT - 1 < wq_lo) && (k0 + KT - 1 < hist);  // no masking needed
@@ -226,17 +240,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     const int kbase_lane = k0 + 8 * g;
     if (uni) {
       const float ub = rab_s[rel_bucket(dmax, nb)];
+      if (full) {
 #pragma unroll
-      for (int mt = 0; mt < KT / 32; ++mt)
+        for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = silu_fast(sacc[mt][r] + ub);
-          if (!full) {
+          for (int r = 0; r < 16; ++r) sacc[mt][r] = silu_l2(fmaf(sacc[mt][r], kLog2e, ub));
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < KT / 32; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int key = kbase_lane + 32 * mt + 16 * (r >> 3) + (r & 7);
-            p = ((key == qpos) || (key < qpos && key < hist)) ? p : 0.f;
+            const float p = silu_l2(fmaf(sacc[mt][r], kLog2e, ub));
+            sacc[mt][r] = (key < vis_lim || key == qpos) ? p : 0.f;
           }
-          sacc[mt][r] = p;
-        }
+      }
     } else {
       const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
 #pragma unroll
@@ -244,10 +262,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
-          float p = silu_fast(sacc[mt][r] + brow[koff]);
           const int key = kbase_lane + koff;
-          p = ((key == qpos) || (key < qpos && key < hist)) ? p : 0.f;
-          sacc[mt][r] = p;
+          const float p = silu_l2(fmaf(sacc[mt][r], kLog2e, brow[koff]));
+          sacc[mt][r] = (key < vis_lim || key == qpos) ? p : 0.f;
         }
     }
 
@@ -273,7 +290,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   }
 
   if (!wave_active) return;
-  // ---- partial tile [BQ][DH] fp32: lane holds column 32 nt + l32, rows 8(r/4)+4g+r%4 ----
+  // ---- partial tile [BQ][DH] fp32 (times log2 e): lane holds column 32 nt + l32,
+  // rows 8(r/4)+4g+r%4 ----
   float* out = a.partials + static_cast<int64_t>(w.slot) * BQ * DH;
 #pragma unroll
   for (int nt = 0; nt < DH / 32; ++nt)

@@ -51,8 +51,8 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void layer_norm_kernel(
 // Each lane owns float4 chunks c = 4 * (lane + 64 k) of the row's H*dh values.
 template <typename T>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
-    PlanDev plan, const float* __restrict__ partials, const T* __restrict__ u, int64_t u_stride,
-    float eps, float* __restrict__ o_out, T* __restrict__ g_out) {
+    PlanDev plan, const float* __restrict__ partials, float o_scale, const T* __restrict__ u,
+    int64_t u_stride, float eps, float* __restrict__ o_out, T* __restrict__ g_out) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= plan.n_new) return;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
   const int qb = plan.row_qblock[row];
   const QBlock blk = plan.qblocks[qb];
   const int local = row - blk.row0;
-  const float inv_n = plan.users[blk.user].inv_n;
+  const float inv_n = plan.users[blk.user].inv_n * o_scale;
   constexpr int kChunks = kMaxPerLane / 4;  // inner <= 64 * 32
   f32x4 o[kChunks];
 #pragma unroll
@@ -133,18 +133,18 @@ hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows,
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials, const void* u,
-                              int64_t u_stride, float eps, float* o_out, void* g_out,
-                              hipStream_t s) {
+hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials,
+                              float o_scale, const void* u, int64_t u_stride, float eps,
+                              float* o_out, void* g_out, hipStream_t s) {
   if (plan.n_new == 0) return hipSuccess;
   if (plan.H * plan.dh > 64 * kMaxPerLane) return hipErrorInvalidValue;
   dim3 grid((plan.n_new + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
   if (dtype == HSTU_BF16)
-    hipLaunchKernelGGL(reduce_gate_kernel<uint16_t>, grid, block, 0, s, plan, partials,
+    hipLaunchKernelGGL(reduce_gate_kernel<uint16_t>, grid, block, 0, s, plan, partials, o_scale,
                        static_cast<const uint16_t*>(u), u_stride, eps, o_out,
                        static_cast<uint16_t*>(g_out));
   else
-    hipLaunchKernelGGL(reduce_gate_kernel<float>, grid, block, 0, s, plan, partials,
+    hipLaunchKernelGGL(reduce_gate_kernel<float>, grid, block, 0, s, plan, partials, o_scale,
                        static_cast<const float*>(u), u_stride, eps, o_out,
                        static_cast<float*>(g_out));
   return hipGetLastError();
