@@ -439,12 +439,14 @@ namespace {
 struct LayerWs {
   size_t xhat, uvqk, partials, g, total;
 };
+// bf16 keeps only the row statistics of x (8 bytes a row) where fp32 keeps
+// the normalised copy
 LayerWs layer_ws(const hstu_plan* p, int dtype, int d_model) {
   const size_t n = static_cast<size_t>(p->n_new), inner = p->desc.num_heads * p->desc.head_dim;
   LayerWs w{};
   size_t off = 0;
   w.xhat = off;
-  off = align256(off + n * d_model * esize(dtype) + 1);
+  off = align256(off + (dtype == HSTU_BF16 ? n * 2 * sizeof(float) : n * d_model * esize(dtype)) + 1);
   w.uvqk = off;
   off = align256(off + n * 4 * inner * esize(dtype) + 1);
   w.partials = off;
@@ -501,12 +503,6 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   const size_t es = esize(a->dtype);
   const int32_t M = p->n_new;
 
-  if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_layer_norm(a->dtype, a->x, xhat, M, d, a->eps, stream); }),
-                      "hstu_layer_forward: pre-norm")) != HSTU_OK)
-    return st;
-  if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_gemm(a->dtype, 0, xhat, a->w1, uvqk, nullptr, M, 4 * inner, d, stream); }),
-                      "hstu_layer_forward: f1")) != HSTU_OK)
-    return st;
   const void* v_new = uvqk + static_cast<size_t>(inner) * es;
   const void* q_new = uvqk + static_cast<size_t>(2 * inner) * es;
   const void* k_new = uvqk + static_cast<size_t>(3 * inner) * es;
@@ -518,20 +514,57 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   L.rab = a->rab;
   L.num_buckets = a->num_buckets;
   L.partials = partials;
-  if (p->desc.page_size > 0) {
+  const bool paged = p->desc.page_size > 0;
+  if (paged) {
     if ((st = fill_keys(L, p, a->dtype, nullptr, nullptr, 0, a->cache, a->layer, a->d_page_table,
                         "hstu_layer_forward")) != HSTU_OK)
-      return st;
-    const hstu_kv_cache* c = a->cache;
-    if ((st = check_hip(timed(TK_APPEND, stream, [&] { return launch_append(a->dtype, &p->dev, p->desc.B, p->dev.new_offsets,
-                                      p->dev.start_pos, a->d_page_table, p->desc.max_pages, k_new,
-                                      v_new, 4 * inner, M, c->k_pool, c->v_pool, a->layer,
-                                      c->num_pages, H, dh, c->page_size, stream); }),
-                        "hstu_layer_forward: append")) != HSTU_OK)
       return st;
   } else {
     if ((st = fill_keys(L, p, a->dtype, k_new, v_new, 4 * inner, nullptr, 0, nullptr,
                         "hstu_layer_forward")) != HSTU_OK)
+      return st;
+  }
+  const hstu_kv_cache* c = a->cache;
+  if (a->dtype == HSTU_BF16) {
+    // row statistics, then f1 with the pre-norm, SiLU and the K/V append fused
+    float* stats = static_cast<float*>(xhat);
+    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, stats, M, d, a->eps, stream); }),
+                        "hstu_layer_forward: row statistics")) != HSTU_OK)
+      return st;
+    F1Args f{};
+    f.uvqk = uvqk;
+    f.inner = inner;
+    f.kv_to_uvqk = a->uvqk_out != nullptr;
+    if (paged) {
+      f.k_pool = c->k_pool;
+      f.v_pool = c->v_pool;
+      f.pool_layer_offset = L.pool_layer_offset;
+      f.page_table = a->d_page_table;
+      f.new_offsets = p->dev.new_offsets;
+      f.start_pos = p->dev.start_pos;
+      f.B = p->desc.B;
+      f.max_pages = p->desc.max_pages;
+      f.num_pages = c->num_pages;
+      f.H = H;
+      f.dh = dh;
+      f.page_size = c->page_size;
+    }
+    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, stats, a->w1, f, M, 4 * inner, d, stream); }),
+                        "hstu_layer_forward: f1")) != HSTU_OK)
+      return st;
+  } else {
+    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_layer_norm(a->dtype, a->x, xhat, M, d, a->eps, stream); }),
+                        "hstu_layer_forward: pre-norm")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_gemm(a->dtype, 0, xhat, a->w1, uvqk, nullptr, M, 4 * inner, d, stream); }),
+                        "hstu_layer_forward: f1")) != HSTU_OK)
+      return st;
+    if (paged &&
+        (st = check_hip(timed(TK_APPEND, stream, [&] { return launch_append(a->dtype, &p->dev, p->desc.B, p->dev.new_offsets,
+                                      p->dev.start_pos, a->d_page_table, p->desc.max_pages, k_new,
+                                      v_new, 4 * inner, M, c->k_pool, c->v_pool, a->layer,
+                                      c->num_pages, H, dh, c->page_size, stream); }),
+                        "hstu_layer_forward: append")) != HSTU_OK)
       return st;
   }
   if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_layer_forward: attention")) != HSTU_OK)

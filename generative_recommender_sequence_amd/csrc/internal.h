@@ -163,7 +163,29 @@ hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows,
                              float eps, hipStream_t s);
 
 // C[M][N] = epilogue(A[M][K] . B[K][N]); epilogue 0: SiLU, 1: + residual R[M][N]
+// (bf16: epilogue 1 only; f1 goes through launch_f1_bf16)
 hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
                        const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s);
+
+// per-row (mean, rstd) of a bf16 [rows][cols] matrix -> float2 [rows]
+hipError_t launch_row_stats(const void* x, float* stats, int32_t rows, int32_t cols, float eps,
+                            hipStream_t s);
+
+// Destinations of the bf16 f1 GEMM's output columns [U|V|Q|K].
+struct F1Args {
+  void* uvqk;             // [M][4 inner]: U and Q always; K and V if kv_to_uvqk or no pools
+  int32_t inner;
+  bool kv_to_uvqk;
+  void* k_pool;           // paged K/V (nullptr: none)
+  void* v_pool;
+  int64_t pool_layer_offset;
+  const int32_t* page_table;
+  const int32_t* new_offsets;
+  const int32_t* start_pos;
+  int32_t B, max_pages, num_pages, H, dh, page_size;
+};
+// [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row stats, routed per F1Args
+hipError_t launch_f1_bf16(const void* x, const float* stats, const void* w1, const F1Args& f,
+                          int32_t M, int32_t N, int32_t K, hipStream_t s);
 
 }  // namespace hstu
