@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 
 #include "internal.h"
@@ -58,7 +59,61 @@ bool tile_visible(int64_t k0, int64_t qa, int64_t qe, int64_t hist) {
   return k0 < hist && k0 < qe - 1;
 }
 
+// Pinned staging for host-to-device uploads, so they are truly asynchronous
+// and the host can plan the next request while the GPU runs this one.  A
+// small ring of pinned buffers, each reused only after its previous copy has
+// completed (an event recorded behind it); buffers grow on demand and live
+// until the process ends.
+struct StagingRing {
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+  };
+  std::mutex mu;
+  Slot slots[4];
+  int next = 0;
+};
+
+StagingRing& staging() {
+  static StagingRing r;
+  return r;
+}
+
 }  // namespace
+
+hstu_status staged_upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return HSTU_OK;
+  StagingRing& r = staging();
+  std::lock_guard<std::mutex> lk(r.mu);
+  StagingRing::Slot& sl = r.slots[r.next];
+  r.next = (r.next + 1) % 4;
+  hstu_status st;
+  if (sl.pending) {
+    if ((st = check_hip(hipEventSynchronize(sl.done), "staged upload")) != HSTU_OK) return st;
+    sl.pending = false;
+  }
+  if (!sl.done && (st = check_hip(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming), "staged upload")) != HSTU_OK)
+    return st;
+  if (sl.cap < bytes) {
+    if (sl.host && (st = check_hip(hipHostFree(sl.host), "staged upload")) != HSTU_OK) return st;
+    sl.host = nullptr;
+    sl.cap = 0;
+    size_t want = std::max(bytes, static_cast<size_t>(1) << 20);
+    if ((st = check_hip(hipHostMalloc(&sl.host, want, hipHostMallocDefault), "staged upload")) != HSTU_OK)
+      return st;
+    sl.cap = want;
+  }
+  std::memcpy(sl.host, src, bytes);
+  if ((st = check_hip(hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream), "staged upload")) !=
+      HSTU_OK)
+    return st;
+  if ((st = check_hip(hipEventRecord(sl.done, stream), "staged upload")) != HSTU_OK) return st;
+  sl.pending = true;
+  return HSTU_OK;
+}
+
 }  // namespace hstu
 
 using namespace hstu;
@@ -281,9 +336,7 @@ hstu_status hstu_plan_upload(hstu_plan* p, void* d_meta, size_t bytes, hipStream
   if (bytes < p->host_blob.size()) return fail(HSTU_ERR_INVALID, "hstu_plan_upload: buffer too small");
   if (reinterpret_cast<uintptr_t>(d_meta) % 256)
     return fail(HSTU_ERR_INVALID, "hstu_plan_upload: d_meta must be 256-byte aligned");
-  hstu_status st = check_hip(hipMemcpyAsync(d_meta, p->host_blob.data(), p->host_blob.size(),
-                                            hipMemcpyHostToDevice, stream),
-                             "hstu_plan_upload");
+  hstu_status st = staged_upload(d_meta, p->host_blob.data(), p->host_blob.size(), stream);
   if (st != HSTU_OK) return st;
   auto* base = static_cast<unsigned char*>(d_meta);
   p->d_meta = d_meta;
@@ -575,6 +628,15 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
     return st;
   return check_hip(timed(TK_F2, stream, [&] { return launch_gemm(a->dtype, 1, g, a->w2, a->y, a->x, M, d, inner, stream); }),
                    "hstu_layer_forward: f2");
+}
+
+hstu_status hstu_stack_forward(const hstu_layer_args* layers, int32_t n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && !layers)) return fail(HSTU_ERR_INVALID, "hstu_stack_forward: bad layer list");
+  for (int32_t i = 0; i < n; ++i) {
+    hstu_status st = hstu_layer_forward(&layers[i], stream);
+    if (st != HSTU_OK) return fail(st, "hstu_stack_forward: layer " + std::to_string(i) + ": " + g_last_error);
+  }
+  return ok();
 }
 
 }  // extern "C"

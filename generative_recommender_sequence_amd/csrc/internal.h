@@ -19,6 +19,8 @@ namespace hstu {
 hstu_status fail(hstu_status st, const std::string& msg);
 hstu_status ok();
 hstu_status check_hip(hipError_t e, const char* what);
+// asynchronous host-to-device copy through a pinned staging buffer
+hstu_status staged_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // ---- tiling constants shared by the plan and the attention kernels --------
 constexpr int kBlockQ = 128;  // queries per attention work item (4 waves x 32)

@@ -84,6 +84,7 @@ SIGNATURES = {
     "hstu_attn_fwd": (c_i32, [ctypes.POINTER(hstu_attn_args), c_vp]),
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
+    "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
     "hstu_timing_enable": (c_i32, [c_i32]),
     "hstu_timing_read": (c_i32, [ctypes.c_char_p, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
@@ -307,6 +308,15 @@ def hstu_layer_workspace_size(args: hstu_layer_args) -> int:
 
 def hstu_layer_forward(args: hstu_layer_args, stream: int):
     _check(lib().hstu_layer_forward(ctypes.byref(args), stream), "hstu_layer_forward")
+
+
+def hstu_stack_forward(layers, stream: int):
+    """layers: a sequence (or ctypes array) of hstu_layer_args."""
+    if not isinstance(layers, ctypes.Array):
+        arr = (hstu_layer_args * len(layers))(*layers)
+    else:
+        arr = layers
+    _check(lib().hstu_stack_forward(arr, len(arr), stream), "hstu_stack_forward")
 
 
 def hstu_timing_enable(enable: bool):

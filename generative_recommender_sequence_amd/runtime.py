@@ -106,10 +106,47 @@ class Request:
             self.plan = 0
 
 
+class RequestBuffers:
+    """Device buffers a stream of requests reuses (page table, plan metadata)
+    and pinned staging for the page-table upload, so that preparing request
+    k+1 on the host never waits for request k on the GPU.  Uploads are
+    ordered on the stream, so reusing the device buffers is safe."""
+
+    def __init__(self, max_batch: int, max_pages: int, meta_bytes: int = 1 << 20, device="cuda", slots: int = 3):
+        self.max_batch, self.max_pages = max_batch, max(max_pages, 1)
+        n = max_batch * self.max_pages
+        self.d_pt = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+        self.d_meta = torch.empty(max(meta_bytes, 256), dtype=torch.uint8, device=device)
+        self.pinned = [torch.empty(max(n, 1), dtype=torch.int32, pin_memory=True) for _ in range(slots)]
+        self.events = [None] * slots
+        self.slot = 0
+
+    def upload_page_table(self, pt: np.ndarray) -> torch.Tensor:
+        n = pt.size
+        k = self.slot
+        self.slot = (self.slot + 1) % len(self.pinned)
+        if self.events[k] is not None:
+            self.events[k].synchronize()
+        self.pinned[k][:n].numpy()[:] = pt.reshape(-1)
+        dst = self.d_pt[:n]
+        dst.copy_(self.pinned[k][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.events[k] = ev
+        return dst.view(pt.shape)
+
+    def meta(self, nbytes: int, device="cuda") -> torch.Tensor:
+        if nbytes > self.d_meta.numel():
+            self.d_meta = torch.empty(2 * nbytes, dtype=torch.uint8, device=device)
+        return self.d_meta
+
+
 def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None, max_pages: int = 0,
-            num_heads: int = 1, head_dim: int = 128, device="cuda", stream=None) -> Request:
+            num_heads: int = 1, head_dim: int = 128, device="cuda", stream=None,
+            bufs: Optional[RequestBuffers] = None) -> Request:
     """Host cache operations (lookup, LRU eviction, allocation), page-table
-    upload, and the request plan, uploaded."""
+    upload, and the request plan, uploaded (asynchronously when `bufs` is
+    given)."""
     users = np.asarray(users, np.int64)
     new_len = np.asarray(new_len, np.int32)
     n_targets = np.asarray(n_targets, np.int32)
@@ -121,7 +158,7 @@ def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None,
         if hstu.kv_free_pages(cache.h) < need:
             evicted = hstu.kv_evict_lru(cache.h, need, users)
         pt, kv_len = hstu.kv_page_alloc(cache.h, users, new_len, max_pages)
-        d_pt = torch.from_numpy(pt).to(device)
+        d_pt = bufs.upload_page_table(pt) if bufs is not None else torch.from_numpy(pt).to(device)
         page_size, num_heads, head_dim = cache.page_size, cache.num_heads, cache.head_dim
     else:
         cached = np.zeros(len(users), np.int32)
@@ -130,7 +167,10 @@ def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None,
     nn = (cached + new_len).astype(np.float32) if norm_n is None else np.asarray(norm_n, np.float32)
     plan = hstu.hstu_plan_create(num_heads, head_dim, new_len, cached, n_targets, nn, page_size, max_pages)
     info = hstu.hstu_plan_get_info(plan)
-    meta = torch.empty(max(int(info.meta_bytes), 256), dtype=torch.uint8, device=device)
+    if bufs is not None:
+        meta = bufs.meta(int(info.meta_bytes), device)
+    else:
+        meta = torch.empty(max(int(info.meta_bytes), 256), dtype=torch.uint8, device=device)
     hstu.hstu_plan_upload(plan, meta.data_ptr(), meta.numel(), s)
     return Request(users, new_len, np.asarray(cached, np.int32), n_targets, nn, np.asarray(kv_len, np.int32),
                    plan, info, meta, d_pt, max_pages, evicted, num_heads, head_dim)
@@ -173,19 +213,23 @@ def workspace_for(model: Model, req: Request, device="cuda") -> torch.Tensor:
 
 def forward(model: Model, req: Request, x: torch.Tensor, cache: Optional[PagedCache],
             workspace: Optional[torch.Tensor] = None, layers: Optional[Sequence[int]] = None,
-            taps: Optional[List[dict]] = None, stream=None) -> torch.Tensor:
-    """Runs the stack on the new tokens x [N_new, d]; returns the last layer's y."""
+            taps: Optional[List[dict]] = None, stream=None,
+            out_bufs: Optional[List[torch.Tensor]] = None) -> torch.Tensor:
+    """Runs the stack on the new tokens x [N_new, d] in one native call
+    (hstu_stack_forward); returns the last layer's y (one of out_bufs)."""
     s = stream_handle(stream)
     if workspace is None:
         workspace = workspace_for(model, req, x.device)
-    layers = range(model.num_layers) if layers is None else layers
-    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    layers = list(range(model.num_layers)) if layers is None else list(layers)
+    if out_bufs is None:
+        out_bufs = [torch.empty_like(x), torch.empty_like(x)]
     cur = x
+    args = []
     for k, li in enumerate(layers):
-        out = bufs[k % 2]
-        a = layer_args(model, req, li, cur, out, cache, workspace, taps[k] if taps else None)
-        hstu.hstu_layer_forward(a, s)
+        out = out_bufs[k % 2]
+        args.append(layer_args(model, req, li, cur, out, cache, workspace, taps[k] if taps else None))
         cur = out
+    hstu.hstu_stack_forward(args, s)
     return cur
 
 

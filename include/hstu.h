@@ -195,8 +195,9 @@ hstu_status hstu_plan_create(const hstu_batch_desc *desc, hstu_plan **out);
 hstu_status hstu_plan_destroy(hstu_plan *plan);
 hstu_status hstu_plan_get_info(const hstu_plan *plan, hstu_plan_info *info);
 /* Copies the schedule to d_meta (device, >= meta_bytes, 256-byte aligned) on
- * `stream`; the plan then refers to d_meta, which must outlive its use.  The
- * plan's host copy stays valid until hstu_plan_destroy. */
+ * `stream`, asynchronously (through pinned staging buffers the library keeps
+ * for the life of the process); the plan then refers to d_meta, which must
+ * outlive its use. */
 hstu_status hstu_plan_upload(hstu_plan *plan, void *d_meta, size_t bytes, hipStream_t stream);
 
 /* ======================================================================== */
@@ -262,6 +263,12 @@ typedef struct {
 
 hstu_status hstu_layer_workspace_size(const hstu_layer_args *args, size_t *bytes);
 hstu_status hstu_layer_forward(const hstu_layer_args *args, hipStream_t stream);
+
+/* The multi-layer stack [DT: 3- and 8-layer models]: hstu_layer_forward on
+ * layers[0..n-1] in order, in one call.  The caller chains the buffers (y of
+ * layer i is x of layer i+1; all layers share the plan).  Stops at the first
+ * failing layer and returns its status (the message names the layer). */
+hstu_status hstu_stack_forward(const hstu_layer_args *layers, int32_t n, hipStream_t stream);
 
 /* ======================================================================== */
 /* Instrumentation: kernel durations measured with HIP events               */

@@ -16,7 +16,7 @@ def test_exports_every_declared_symbol():
     assert len(syms) >= 20
     for s in syms:
         assert hasattr(L, s), s
-    assert set(syms) == set(hstu.SIGNATURES)
+    assert set(syms) == set(hstu.SIGNATURES), set(syms) ^ set(hstu.SIGNATURES)
     assert L.hstu_abi_version() == 1
 
 
