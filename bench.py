@@ -82,7 +82,7 @@ def main(argv=None):
 
     import torch
 
-    from generative_recommender_sequence_amd import hstu, runtime
+    from generative_recommender_sequence_amd import hstu, profiling, runtime
     from generative_recommender_sequence_amd.workloads import workload_for
 
     runtime.require_gpu()
@@ -165,6 +165,8 @@ def main(argv=None):
         achieved = flops / (att_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    traffic = profiling.read_traffic(args.workload)
+    roof["traffic"] = None if traffic is None else round(traffic, 0)
     roof.update({"kernel": "attention (attn_bf16_kernel, paged)", "avg_us": att_us,
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
                  "unmasked_pairs_per_head": int(req_last.info.pairs)})

@@ -2,6 +2,7 @@
 
     python -m generative_recommender_sequence_amd.profiling trace DIR
     python -m generative_recommender_sequence_amd.profiling pmc DIR [--copy DIR]
+    python -m generative_recommender_sequence_amd.profiling traffic WORKLOAD FETCH_DIR WRITE_DIR --copy DIR
 
 `trace` reads the *_kernel_trace.csv under DIR (rocprofv3 --kernel-trace
 --output-format csv) and prints per (kernel, grid size) the number of
@@ -15,6 +16,12 @@ prints per (kernel, grid size) the mean of every counter.  With --copy DIR2
 `bench.py --calibrate-copy BYTES`), FETCH_SIZE / WRITE_SIZE are also scaled
 by the ratio between the bytes the copy moved and what the counter read for
 it, giving HBM bytes per dispatch.
+
+`traffic` prints one line for the attention-traffic table the benchmark
+reads: the workload, the grid of its timed attention launch (the attention
+grid with the most dispatches), the calibrated FETCH_SIZE and WRITE_SIZE bytes
+per launch, and a hash of the sources that decide what that launch reads and
+writes.  The benchmark reports the figure only while the hash still matches.
 """
 from __future__ import annotations
 
@@ -22,8 +29,36 @@ import argparse
 import collections
 import csv
 import glob
+import hashlib
 import os
 import sys
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+# the attention kernel and the host scheduler that sizes its work items
+TRAFFIC_SOURCES = ("csrc/kernels/attention.hip", "csrc/kernels/common.h", "csrc/internal.h",
+                   "csrc/hstu_abi.cpp")
+TRAFFIC_TABLE = os.path.join(os.path.dirname(_PKG), "profiles", "attention_traffic.txt")
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(_PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """Calibrated HBM bytes (fetch + write) of the workload's attention launch,
+    or None when the table has no line for it or the sources changed since."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    cur = sources_hash()
+    for line in open(TRAFFIC_TABLE):
+        f = line.split()
+        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[4] == cur:
+            return float(f[2]) + float(f[3])
+    return None
 
 
 def _files(d, suffix):
@@ -84,8 +119,9 @@ def copy_factor(d: str, counter: str, bytes_moved: int) -> float:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["trace", "pmc"])
-    ap.add_argument("dir")
+    ap.add_argument("mode", choices=["trace", "pmc", "traffic"])
+    ap.add_argument("dir", help="trace/pmc: the output directory; traffic: the workload name")
+    ap.add_argument("more", nargs="*", help="traffic: FETCH_SIZE and WRITE_SIZE directories")
     ap.add_argument("--copy", default=None, help="pmc directory of the calibration copy")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     a = ap.parse_args(argv)
@@ -94,6 +130,17 @@ def main(argv=None):
         print("|---|---:|---:|---:|---:|---:|---:|")
         for k, grid, n, avg, mn, mx, tot in trace_summary(a.dir):
             print(f"| {k} | {grid} | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {tot:.1f} |")
+        return
+    if a.mode == "traffic":
+        fdir, wdir = a.more
+        fac = {c: copy_factor(os.path.join(a.copy, c), c, a.copy_bytes) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        per = {}
+        for c, d in (("FETCH_SIZE", fdir), ("WRITE_SIZE", wdir)):
+            for (k, grid), (n, agg) in pmc_summary(d).items():
+                if "attn_bf16_kernel" in k and c in agg:
+                    per.setdefault(grid, {"n": n})[c] = agg[c] * 1024 * fac[c]
+        grid = max(per, key=lambda g: per[g]["n"])
+        print(f"{a.dir} {grid} {per[grid]['FETCH_SIZE']:.0f} {per[grid]['WRITE_SIZE']:.0f} {sources_hash()}")
         return
     fac = {}
     if a.copy:
