@@ -63,7 +63,7 @@ constexpr int kMaxBuckets = 256;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ v4i16 lds_read_tr(const __attribute__((address_space(3))) uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
@@ -77,11 +77,38 @@ __device__ __forceinline__ float silu_l2(float y) {
   return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y));
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef const __attribute__((address_space(1))) void global_void;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// dst + 16 l (dst is wave-uniform), without passing through registers.
+__device__ __forceinline__ void dma16(const uint16_t* src, lds_u16* dst) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ bool block_uniform_bias(int k0, int qa, int qe, int nb) {
+  const int dlo = qa - (k0 + KT - 1), dhi = qe - 1 - k0;
+  return dlo >= 0 && rel_bucket(dlo, nb) == rel_bucket(dhi, nb);
+}
+
+// K/V tiles are double-buffered in LDS: while the waves multiply tile t out
+// of one buffer, the copy engine fills the other with the next visible tile,
+// so each tile costs one barrier and no register staging.  The buffers are
+// separate LDS objects and each loop half names its own, so the compiler can
+// tell the in-flight copy does not touch the buffer being read.
 template <bool PAGED>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * DH];
-  __shared__ float bias_rev[256];     // log2(e) * bias, reversed distance order
+  __shared__ __attribute__((aligned(16))) uint16_t K0s[KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t V0s[KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t K1s[KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t V1s[KT * DH];
+  lds_u16* const K0 = (lds_u16*)K0s;
+  lds_u16* const V0 = (lds_u16*)V0s;
+  lds_u16* const K1 = (lds_u16*)K1s;
+  lds_u16* const V1 = (lds_u16*)V1s;
+  __shared__ float bias0[256];          // log2(e) * bias, reversed distance order
+  __shared__ float bias1[256];
   __shared__ float rab_s[kMaxBuckets];  // log2(e) * rab
   __shared__ int32_t pages_lds[PAGED ? kMaxPagesLds : 1];
 
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   // ---- stage the bias table and this work item's page-table slice ----
   for (int i = tid; i < nb; i += 256) rab_s[i] = a.rab[i] * kLog2e;
   const int P = PAGED ? a.plan.page_size : KT;
-  const int p_shift = __ffs(P) - 1;          // the host guarantees a power of two
+  const int p_shift = __ffs(P) - 1;          // the host guarantees a power of two >= 16
   int pg0 = 0;
   if (PAGED) {
     pg0 = (w.tile_begin * KT) >> p_shift;
@@ -133,41 +160,64 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
   for (int t = 0; t < DH / 32; ++t) oacc[t] = f32x16{};
 
-  // ---- loader: rows lr + 16 i (i < 4) of a tile, 16-byte chunk lc ----
-  // The 4 rows a wave loads per i are consecutive, so for pages of 16+
-  // tokens they share one page: the row-group base is scalar and each lane
-  // adds a constant offset.
-  const int lc = tid & 15, lr = tid >> 4;
-  const int pm = P < KT ? P : KT;
-  int loff[4];
+  // ---- tile copy: wave w fills rows 16 w .. 16 w + 15, four rows per
+  // instruction; lane l of instruction i carries row 16 w + 4 i + l / 16,
+  // LDS chunk slot l % 16, which holds global chunk slot ^ swizzle(row). ----
+  const int lrow = lane >> 4, lslot = lane & 15;
+  const int64_t row_stride = PAGED ? DH : a.kv_stride;
+  int loffk[4], loffv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = lr + 16 * i;
-    loff[i] = PAGED ? (r & (pm - 1)) * DH + 8 * lc
-                    : r * static_cast<int>(a.kv_stride) + h * DH + 8 * lc;
+    const int r = 4 * i + lrow;  // row within the wave's 16 (swizzles only see row & 15)
+    loffk[i] = static_cast<int>(r * row_stride) + 8 * (lslot ^ kswz(r));
+    loffv[i] = static_cast<int>(r * row_stride) + 8 * (lslot ^ vswz(r));
   }
-  u32x4 kreg[4], vreg[4];
-  auto fetch = [&](int tile) {
+  auto copy_tile = [&](int tile, lds_u16* Kd, lds_u16* Vd) {
     const int k0 = tile * KT;
-    const bool tail = k0 + KT > ui.kv_len;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    const int r0 = k0 + 16 * wave;  // first key of this wave's rows
+    if (r0 + 16 <= ui.kv_len) {
       int64_t base;
-      bool ok = !tail || (k0 + lr + 16 * i < ui.kv_len);
       if (PAGED) {
-        const int lp = (k0 + 16 * i + 4 * wave) >> p_shift;
-        const int page = uniform(pages_lds[lp - pg0]);
-        ok = ok && page >= 0 && page < a.num_pages;
-        base = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (k0 & (P - 1))) * DH;
+        int page = uniform(pages_lds[(r0 >> p_shift) - pg0]);
+        page = (page >= 0 && page < a.num_pages) ? page : 0;
+        base = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (r0 & (P - 1))) * DH;
       } else {
-        base = static_cast<int64_t>(ui.kv_row0 + k0) * a.kv_stride;
+        base = static_cast<int64_t>(ui.kv_row0 + r0) * a.kv_stride + h * DH;
       }
-      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(kbase + base + loff[i]) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(vbase + base + loff[i]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dma16(kbase + base + loffk[i], Kd + (16 * wave + 4 * i) * DH);
+        dma16(vbase + base + loffv[i], Vd + (16 * wave + 4 * i) * DH);
+      }
+    } else {
+      // rows past the user's last key repeat that key: finite values whose
+      // weights the mask zeroes
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + lrow;
+        const int key = min(r0 + r, ui.kv_len - 1);
+        int64_t off;
+        if (PAGED) {
+          int page = pages_lds[(key >> p_shift) - pg0];
+          page = (page >= 0 && page < a.num_pages) ? page : 0;
+          off = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (key & (P - 1))) * DH;
+        } else {
+          off = static_cast<int64_t>(ui.kv_row0 + key) * a.kv_stride + h * DH;
+        }
+        dma16(kbase + off + 8 * (lslot ^ kswz(r)), Kd + (16 * wave + 4 * i) * DH);
+        dma16(vbase + off + 8 * (lslot ^ vswz(r)), Vd + (16 * wave + 4 * i) * DH);
+      }
+    }
+  };
+  auto fill_bias = [&](int tile, float* bias_rev) {
+    const int k0 = tile * KT;
+    if (!block_uniform_bias(k0, qa, qe, nb) && tid < kBiasLen) {
+      const int d = qa + BQ - 1 - k0 - tid;
+      bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
     }
   };
 
-  // per-lane LDS read addresses (elements), hoisted out of the tile loop
+  // per-lane LDS read offsets (elements), hoisted out of the tile loop
   int kaddr[DH / 16];  // A operand of S^T: row vperm(l32) (+32 per row block), chunk (2s+g)
   {
     const int row = vperm(l32);
@@ -189,37 +239,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     }
   }
 
-  auto visible_tile = [&](int t) { return tile_visible_dev(t * KT, qa, qe, hist); };
-  int t = w.tile_begin;
-  while (t < w.tile_end && !visible_tile(t)) ++t;
-  __syncthreads();  // rab and page-table slice staged
-  if (t < w.tile_end) fetch(t);
-
-  while (t < w.tile_end) {
-    int tn = t + 1;
-    while (tn < w.tile_end && !visible_tile(tn)) ++tn;
+  auto compute_tile = [&](int t, const lds_u16* Ks, const lds_u16* Vs, const float* bias_rev) {
     const int k0 = t * KT;
-    // distances this block's queries see in this tile; one bucket -> no table
-    const int blk_dlo = qa - (k0 + KT - 1), blk_dhi = qe - 1 - k0;
-    const bool blk_uni = blk_dlo >= 0 && rel_bucket(blk_dlo, nb) == rel_bucket(blk_dhi, nb);
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = lr + 16 * i;
-      *reinterpret_cast<u32x4*>(&Ks[row * DH + 8 * (lc ^ kswz(row))]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[row * DH + 8 * (lc ^ vswz(row))]) = vreg[i];
-    }
-    if (!blk_uni && tid < kBiasLen) {
-      const int d = qa + BQ - 1 - k0 - tid;
-      bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
-    }
-    __syncthreads();
-    if (tn < w.tile_end) fetch(tn);  // in flight while this tile is computed
-    if (!wave_active) {
-      t = tn;
-      continue;
-    }
-
     // ---- S^T = K . Q^T (register r of block mt: key 32 mt + 16 (r/8) + 8 g + r%8) ----
     f32x16 sacc[KT / 32];
 #pragma unroll
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
       sacc[mt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < DH / 16; ++s) {
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[kaddr[s] + 32 * mt * DH]);
+        bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(&Ks[kaddr[s] + 32 * mt * DH]);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[mt], 0, 0, 0);
       }
     }
@@ -286,6 +307,43 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
         oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[nt], 0, 0, 0);
       }
     }
+  };
+
+  auto visible_tile = [&](int t) { return tile_visible_dev(t * KT, qa, qe, hist); };
+  auto next_visible = [&](int t) {
+    ++t;
+    while (t < w.tile_end && !visible_tile(t)) ++t;
+    return t;
+  };
+  int t = w.tile_begin;
+  while (t < w.tile_end && !visible_tile(t)) ++t;
+  __syncthreads();  // rab and page-table slice staged
+  if (t < w.tile_end) {
+    copy_tile(t, K0, V0);
+    fill_bias(t, bias0);
+  }
+  __syncthreads();  // tile t in buffer 0
+
+  // two tiles per trip so that each half names its buffers statically
+  while (t < w.tile_end) {
+    int tn = next_visible(t);
+    if (tn < w.tile_end) {
+      copy_tile(tn, K1, V1);
+      fill_bias(tn, bias1);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // issue the copy before the tile's LDS reads
+    if (wave_active) compute_tile(t, K0, V0, bias0);
+    __syncthreads();  // buffer 1 filled; buffer 0 free
+    if (tn >= w.tile_end) break;
+    t = tn;
+    tn = next_visible(t);
+    if (tn < w.tile_end) {
+      copy_tile(tn, K0, V0);
+      fill_bias(tn, bias0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave_active) compute_tile(t, K1, V1, bias1);
+    __syncthreads();  // buffer 0 filled; buffer 1 free
     t = tn;
   }
 
