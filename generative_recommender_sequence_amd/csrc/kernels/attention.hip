@@ -87,9 +87,12 @@ __device__ __forceinline__ void dma16(const uint16_t* src, lds_u16* dst) {
   __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ bool block_uniform_bias(int k0, int qa, int qe, int nb) {
+// The per-tile bias table is needed unless every query of the block sees the
+// whole tile (no mask) at distances that fall in one bucket.
+__device__ __forceinline__ bool needs_bias_table(int k0, int qa, int qe, int hist, int nb) {
   const int dlo = qa - (k0 + KT - 1), dhi = qe - 1 - k0;
-  return dlo >= 0 && rel_bucket(dlo, nb) == rel_bucket(dhi, nb);
+  const bool unmasked = k0 + KT - 1 < qa && k0 + KT - 1 < hist;
+  return !(unmasked && rel_bucket(dlo, nb) == rel_bucket(dhi, nb));
 }
 
 // K/V tiles are double-buffered in LDS: while the waves multiply tile t out
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   };
   auto fill_bias = [&](int tile, float* bias_rev) {
     const int k0 = tile * KT;
-    if (!block_uniform_bias(k0, qa, qe, nb) && tid < kBiasLen) {
+    if (needs_bias_table(k0, qa, qe, hist, nb) && tid < kBiasLen) {
       const int d = qa + BQ - 1 - k0 - tid;
       bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
     }
@@ -259,25 +262,25 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     const bool full = (k0 + KT - 1 < wq_lo) && (k0 + KT - 1 < hist);  // no masking needed
     const bool uni = dmin >= 0 && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
     const int kbase_lane = k0 + 8 * g;
-    if (uni) {
+    // three cases, in falling order of frequency: far tiles with one bias
+    // value, far tiles spanning bucket edges (bias table, no mask), and tiles
+    // on the diagonal or the candidate block (bias table and mask)
+    const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
+    if (full && uni) {
       const float ub = rab_s[rel_bucket(dmax, nb)];
-      if (full) {
 #pragma unroll
-        for (int mt = 0; mt < KT / 32; ++mt)
+      for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[mt][r] = silu_l2(fmaf(sacc[mt][r], kLog2e, ub));
-      } else {
+        for (int r = 0; r < 16; ++r) sacc[mt][r] = silu_l2(fmaf(sacc[mt][r], kLog2e, ub));
+    } else if (full) {
 #pragma unroll
-        for (int mt = 0; mt < KT / 32; ++mt)
+      for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase_lane + 32 * mt + 16 * (r >> 3) + (r & 7);
-            const float p = silu_l2(fmaf(sacc[mt][r], kLog2e, ub));
-            sacc[mt][r] = (key < vis_lim || key == qpos) ? p : 0.f;
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
+          sacc[mt][r] = silu_l2(fmaf(sacc[mt][r], kLog2e, brow[koff]));
+        }
     } else {
-      const float* brow = &bias_rev[BQ - 1 - qlocal + 8 * g];
 #pragma unroll
       for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
@@ -319,8 +322,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   while (t < w.tile_end && !visible_tile(t)) ++t;
   __syncthreads();  // rab and page-table slice staged
   if (t < w.tile_end) {
-    copy_tile(t, K0, V0);
     fill_bias(t, bias0);
+    copy_tile(t, K0, V0);
   }
   __syncthreads();  // tile t in buffer 0
 
@@ -328,8 +331,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   while (t < w.tile_end) {
     int tn = next_visible(t);
     if (tn < w.tile_end) {
-      copy_tile(tn, K1, V1);
       fill_bias(tn, bias1);
+      copy_tile(tn, K1, V1);
     }
     __builtin_amdgcn_sched_barrier(0);  // issue the copy before the tile's LDS reads
     if (wave_active) compute_tile(t, K0, V0, bias0);
@@ -338,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     t = tn;
     tn = next_visible(t);
     if (tn < w.tile_end) {
-      copy_tile(tn, K0, V0);
       fill_bias(tn, bias0);
+      copy_tile(tn, K0, V0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (wave_active) compute_tile(t, K1, V1, bias1);
