@@ -490,16 +490,19 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
 
 namespace {
 struct LayerWs {
-  size_t xhat, uvqk, partials, g, total;
+  size_t xhat, colsum, uvqk, partials, g, total;
 };
-// bf16 keeps only the row statistics of x (8 bytes a row) where fp32 keeps
-// the normalised copy
+// bf16 keeps only the row statistics of x (8 bytes a row) and the column sums
+// of W1 where fp32 keeps the normalised copy
 LayerWs layer_ws(const hstu_plan* p, int dtype, int d_model) {
   const size_t n = static_cast<size_t>(p->n_new), inner = p->desc.num_heads * p->desc.head_dim;
   LayerWs w{};
   size_t off = 0;
   w.xhat = off;
-  off = align256(off + (dtype == HSTU_BF16 ? n * 2 * sizeof(float) : n * d_model * esize(dtype)) + 1);
+  // bf16: row records [n] (statistics and page slot), then the f1 column sums [4 inner] fp32
+  w.colsum = align256(off + n * sizeof(RowInfo) + 1);
+  off = dtype == HSTU_BF16 ? align256(w.colsum + 4 * inner * sizeof(float) + 1)
+                           : align256(off + n * d_model * esize(dtype) + 1);
   w.uvqk = off;
   off = align256(off + n * 4 * inner * esize(dtype) + 1);
   w.partials = off;
@@ -580,29 +583,34 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   const hstu_kv_cache* c = a->cache;
   if (a->dtype == HSTU_BF16) {
     // row statistics, then f1 with the pre-norm, SiLU and the K/V append fused
-    float* stats = static_cast<float*>(xhat);
-    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, stats, M, d, a->eps, stream); }),
-                        "hstu_layer_forward: row statistics")) != HSTU_OK)
-      return st;
+    // row records (statistics, page slots) and W1's column sums, then f1 with
+    // the pre-norm, SiLU and the K/V append fused
+    auto* info = static_cast<RowInfo*>(xhat);
+    float* colsum = reinterpret_cast<float*>(ws + w.colsum);
     F1Args f{};
     f.uvqk = uvqk;
     f.inner = inner;
     f.kv_to_uvqk = a->uvqk_out != nullptr;
+    f.dh = dh;
+    RowPages pg{};
     if (paged) {
       f.k_pool = c->k_pool;
       f.v_pool = c->v_pool;
       f.pool_layer_offset = L.pool_layer_offset;
-      f.page_table = a->d_page_table;
-      f.new_offsets = p->dev.new_offsets;
-      f.start_pos = p->dev.start_pos;
-      f.B = p->desc.B;
-      f.max_pages = p->desc.max_pages;
-      f.num_pages = c->num_pages;
-      f.H = H;
-      f.dh = dh;
       f.page_size = c->page_size;
+      pg.page_table = a->d_page_table;
+      pg.row_qblock = p->dev.row_qblock;
+      pg.qblocks = p->dev.qblocks;
+      pg.max_pages = p->desc.max_pages;
+      pg.num_pages = c->num_pages;
+      pg.H = H;
+      pg.dh = dh;
+      pg.page_size = c->page_size;
     }
-    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, stats, a->w1, f, M, 4 * inner, d, stream); }),
+    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, info, M, d, a->eps, a->w1, colsum, 4 * inner, pg, stream); }),
+                        "hstu_layer_forward: row statistics")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, info, colsum, a->w1, f, M, 4 * inner, d, stream); }),
                         "hstu_layer_forward: f1")) != HSTU_OK)
       return st;
   } else {

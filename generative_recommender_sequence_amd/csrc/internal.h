@@ -164,13 +164,30 @@ inline float partial_scale(int dtype) { return dtype == HSTU_BF16 ? kBf16Partial
 hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows, int32_t cols,
                              float eps, hipStream_t s);
 
-// C[M][N] = epilogue(A[M][K] . B[K][N]); epilogue 0: SiLU, 1: + residual R[M][N]
+// C[M][N] = epilogue(A[M][K] . Wt[N][K]^T); epilogue 0: SiLU, 1: + residual R[M][N]
 // (bf16: epilogue 1 only; f1 goes through launch_f1_bf16)
 hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
                        const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s);
 
-// per-row (mean, rstd) of a bf16 [rows][cols] matrix -> float2 [rows]
-hipError_t launch_row_stats(const void* x, float* stats, int32_t rows, int32_t cols, float eps,
+// Per new-token row of the bf16 path: LayerNorm statistics of x and the
+// element offset, within one layer of the pools, of the row's (page, head 0,
+// slot) for the K/V append (-1: not appended).
+struct RowInfo {
+  float mean, rstd;
+  int64_t pool_row;
+};
+// Paging of the new tokens (page_table == nullptr: none); rows are mapped to
+// (user, position) through the plan's q-blocks.
+struct RowPages {
+  const int32_t* page_table;   // [B][max_pages]
+  const int32_t* row_qblock;   // [n_new]
+  const QBlock* qblocks;
+  int32_t max_pages, num_pages, H, dh, page_size;
+};
+// RowInfo of each row of a bf16 [rows][cols] matrix, and in the same launch
+// the row sums of w1t (bf16 [w1t_rows][cols]) -> colsum
+hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
+                            const void* w1t, float* colsum, int32_t w1t_rows, const RowPages& pg,
                             hipStream_t s);
 
 // Destinations of the bf16 f1 GEMM's output columns [U|V|Q|K].
@@ -178,16 +195,13 @@ struct F1Args {
   void* uvqk;             // [M][4 inner]: U and Q always; K and V if kv_to_uvqk or no pools
   int32_t inner;
   bool kv_to_uvqk;
-  void* k_pool;           // paged K/V (nullptr: none)
+  void* k_pool;           // paged K/V (nullptr: none), rows placed by RowInfo::pool_row
   void* v_pool;
   int64_t pool_layer_offset;
-  const int32_t* page_table;
-  const int32_t* new_offsets;
-  const int32_t* start_pos;
-  int32_t B, max_pages, num_pages, H, dh, page_size;
+  int32_t dh, page_size;
 };
 // [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row stats, routed per F1Args
-hipError_t launch_f1_bf16(const void* x, const float* stats, const void* w1, const F1Args& f,
-                          int32_t M, int32_t N, int32_t K, hipStream_t s);
+hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
+                          const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s);
 
 }  // namespace hstu

@@ -2,25 +2,26 @@
 // Redefining RecSys at Scale", section HSTU):
 //   f1: [U|V|Q|K] = SiLU(LayerNorm(x) . W1)   (epilogue 0)
 //   f2: y = x + g . W2                        (epilogue 1)
-// Matrices are row-major: A [M][K], B [K][N] (the weight layout), C [M][N].
+// A is row-major [M][K]; the weights come output-major, Wt [N][K] (the
+// transpose of the x . W layout), so both operands are rows of contiguous k.
 //
-// bf16 kernel: a BM x 128 output tile per 256-thread block (4 waves as 2 x 2,
-// each wave (BM/2) x 64 as v_mfma_f32_32x32x16_bf16 tiles), K staged 64 at a
-// time through LDS.  Each MFMA multiplies a W^T fragment by an x^T fragment,
-// producing C^T tiles, so a lane owns 4 consecutive output columns of one row
-// and stores (and reads the residual) 8 bytes at a time.  B tiles are written
-// to LDS transposed (n-major) because the MFMA wants 8 consecutive k per lane;
-// both LDS tiles use a 16-byte-chunk XOR swizzle so the transposing writes and
-// the operand reads are free of bank conflicts.  The next K tile is fetched
-// into registers while the current one is multiplied.
+// bf16 kernel: a BM x BN output tile per 256-thread block (4 waves as 2 x 2,
+// each wave (BM/2) x (BN/2) as v_mfma_f32_32x32x16_bf16 tiles), K in steps of
+// 64.  Both operand tiles are double-buffered in LDS and filled by direct
+// global -> LDS copies (no register staging, one barrier per k step); rows are
+// 64 k wide with a 16-byte-chunk XOR swizzle that keeps the 16-lane operand
+// reads free of bank conflicts.  Each MFMA multiplies a Wt fragment by an x
+// fragment, producing C^T tiles, so a lane owns 4 consecutive output columns
+// of one row and stores (and reads the residual) 8 bytes at a time.  Blocks
+// are dealt to the 8 XCDs so that the n tiles of one m tile share an L2.
 //
 // Epilogue 0 applies the pre-norm algebraically: with mu, rstd the row
-// statistics of x and s_n = sum_k W1[k][n],
+// statistics of x and s_n = sum_k W1[k][n] (computed with the statistics),
 //     LayerNorm(x) . W1 = rstd * (x . W1 - mu * s_n),
-// so x is multiplied as stored (no normalised copy) and s_n is accumulated
-// while W1 is staged.  The SiLU'd columns are routed by chunk: U and Q to the
-// token-major buffer, K and V either to the same buffer (contiguous keys) or
-// straight into their pages (paged cache; the append of the new tokens).
+// so x is multiplied as stored (no normalised copy).  The SiLU'd columns are
+// routed by chunk: U and Q to the token-major buffer, K and V either to the
+// same buffer (contiguous keys) or straight into their pages (paged cache; the
+// append of the new tokens).
 //
 // fp32: plain 64 x 64-tile FMA kernels, with the pre-norm done by a separate
 // row LayerNorm and the append by the copy kernel.
@@ -29,137 +30,151 @@
 namespace hstu {
 namespace {
 
-constexpr int GBN = 128, GBK = 64;
+constexpr int GBK = 64;
 
-__device__ __forceinline__ float epi_silu(float x) { return x / (1.0f + __expf(-x)); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef const __attribute__((address_space(1))) void global_void;
 
-__device__ __forceinline__ int swz_a(int m, int c) { return c ^ (m & 7); }
-__device__ __forceinline__ int swz_b(int n, int c) { return c ^ ((n + (n >> 3)) & 7); }
+__device__ __forceinline__ void dma16(const uint16_t* src, lds_u16* dst) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
+// 16-byte chunk slot of logical chunk c in row r of a 64-wide tile (rows are
+// 128 B, two per 64 banks): 16 consecutive rows read at one logical chunk hit
+// 16 distinct bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // Routing of f1's output columns (epilogue 0).
 struct F1Route {
-  const float2* stats;       // [M] (mean, rstd) of the input rows
-  uint16_t* uvqk;            // [M][4 inner] token-major destination
-  int32_t inner;             // H * dh
-  bool kv_to_uvqk;           // also write the K and V chunks to uvqk
-  // paged K/V destination (k_pool == nullptr: none)
-  uint16_t* k_pool;
+  const RowInfo* rows;        // [M] statistics and page slot of the input rows
+  const float* colsum;        // [N] column sums of W1
+  uint16_t* uvqk;             // [M][4 inner] token-major destination
+  int32_t inner;              // H * dh
+  bool kv_to_uvqk;            // also write the K and V chunks to uvqk
+  uint16_t* k_pool;           // paged K/V destination (nullptr: none)
   uint16_t* v_pool;
   int64_t pool_layer_offset;  // elements
-  const int32_t* page_table;  // [B][max_pages]
-  const int32_t* new_offsets; // [B+1]
-  const int32_t* start_pos;   // [B]
-  int32_t B, max_pages, num_pages, H, dh, page_size;
+  int32_t dh, page_size;
 };
 
-template <int BM, int EPI>
+template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                           const uint16_t* __restrict__ Bm,
+                                                           const uint16_t* __restrict__ Wt,
                                                            uint16_t* __restrict__ C,
                                                            const uint16_t* __restrict__ R,
                                                            F1Route route, int32_t M, int32_t N,
                                                            int32_t K) {
-  constexpr int MT = BM / 64;  // 32-row MFMA tiles per wave along m
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * GBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bt[GBN * GBK];
-  __shared__ float colsum_part[EPI == 0 ? 16 * GBN : 1];
+  constexpr int MT = BM / 64, NT = BN / 64;  // 32-wide MFMA tiles per wave along m, n
+  __shared__ __attribute__((aligned(16))) uint16_t A0s[BM * GBK];
+  __shared__ __attribute__((aligned(16))) uint16_t A1s[BM * GBK];
+  __shared__ __attribute__((aligned(16))) uint16_t B0s[BN * GBK];
+  __shared__ __attribute__((aligned(16))) uint16_t B1s[BN * GBK];
+  lds_u16* const A0 = (lds_u16*)A0s;
+  lds_u16* const A1 = (lds_u16*)A1s;
+  lds_u16* const B0 = (lds_u16*)B0s;
+  lds_u16* const B1 = (lds_u16*)B1s;
+
+  // XCD-aware tile order: block b runs on XCD b % 8 (the grid is a multiple
+  // of 8); XCD x takes tiles x * per_xcd .. , n fastest.
+  const int n_tiles_n = N / BN;
+  const int tiles = ((M + BM - 1) / BM) * n_tiles_n;
+  const int per_xcd = gridDim.x / 8;
+  const int id = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (id >= tiles) return;
+  const int m0 = (id / n_tiles_n) * BM;
+  const int n0 = (id % n_tiles_n) * BN;
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n_tiles_n = N / GBN;
-  const int m0 = (blockIdx.x / n_tiles_n) * BM;
-  const int n0 = (blockIdx.x % n_tiles_n) * GBN;
 
-  // global -> register staging: A: rows tid/8 + 32 i, chunk tid%8;
-  // B: 2 rounds x 2 rows (k pair 2*(tid/16) + 32 r), n chunk tid%16
-  u32x4 ra[BM / 32], rb[4];
-  float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto load_tiles = [&](int k0) {
+  // copy: instruction j of the block fills rows 8 j .. 8 j + 7 (1 KB); lane l
+  // carries row 8 j + l / 8, chunk slot l % 8, i.e. logical chunk slot ^ swz8(row)
+  const int crow = lane >> 3, cslot = lane & 7;
+  auto copy_k = [&](int k0, lds_u16* Ad, lds_u16* Bd) {
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) {
-      int m = m0 + tid / 8 + 32 * i;
-      int c = tid % 8;
-      ra[i] = m < M ? *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m) * K + k0 + 8 * c)
-                    : u32x4{0u, 0u, 0u, 0u};
+      const int r = 8 * (wave + 4 * i) + crow;
+      const int m = min(m0 + r, M - 1);  // rows past M repeat the last row
+      dma16(A + static_cast<int64_t>(m) * K + k0 + 8 * (cslot ^ swz8(r)), Ad + 8 * (wave + 4 * i) * GBK);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      int k = k0 + 2 * (tid / 16) + 32 * r;
-      int n = n0 + 8 * (tid % 16);
-      rb[2 * r] = *reinterpret_cast<const u32x4*>(Bm + static_cast<int64_t>(k) * N + n);
-      rb[2 * r + 1] = *reinterpret_cast<const u32x4*>(Bm + static_cast<int64_t>(k + 1) * N + n);
-    }
-  };
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) {
-      int m = tid / 8 + 32 * i, c = tid % 8;
-      *reinterpret_cast<u32x4*>(&As[m * GBK + 8 * swz_a(m, c)]) = ra[i];
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      int kk = 2 * (tid / 16) + 32 * r;  // even k within the tile
-      int nb = 8 * (tid % 16);
-      u32x4 lo = rb[2 * r], hi = rb[2 * r + 1];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t a = (j & 1) ? (lo[j >> 1] >> 16) : (lo[j >> 1] & 0xFFFFu);
-        uint32_t b = (j & 1) ? (hi[j >> 1] >> 16) : (hi[j >> 1] & 0xFFFFu);
-        if (EPI == 0) csum[j] += bf2f(static_cast<uint16_t>(a)) + bf2f(static_cast<uint16_t>(b));
-        int n = nb + j;
-        int chunk = swz_b(n, kk >> 3);
-        *reinterpret_cast<uint32_t*>(&Bt[n * GBK + 8 * chunk + (kk & 7)]) = a | (b << 16);
-      }
+    for (int i = 0; i < BN / 32; ++i) {
+      const int r = 8 * (wave + 4 * i) + crow;
+      dma16(Wt + static_cast<int64_t>(n0 + r) * K + k0 + 8 * (cslot ^ swz8(r)), Bd + 8 * (wave + 4 * i) * GBK);
     }
   };
 
-  f32x16 acc[MT][2];
+  // operand reads: row (wave half) + 32 t + l32, logical chunk 2 ks + g; the
+  // swizzle only sees l32 (the other row terms are multiples of 16)
+  int koff[GBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < GBK / 16; ++ks) koff[ks] = l32 * GBK + 8 * ((2 * ks + g) ^ swz8(l32));
+  const int a_row0 = wm * (BM / 2) * GBK, b_row0 = wn * (BN / 2) * GBK;
+
+  f32x16 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-  const int nk = K / GBK;
-  load_tiles(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store_tiles();
-    __syncthreads();
-    if (kt + 1 < nk) load_tiles((kt + 1) * GBK);
+  auto mma_k = [&](const lds_u16* As, const lds_u16* Bs) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[MT], bfr[2];
+      bf16x8 af[MT], bfr[NT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        int m = wm * (BM / 2) + 32 * i + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[m * GBK + 8 * swz_a(m, 2 * ks + g)]);
-      }
+      for (int i = 0; i < MT; ++i)
+        af[i] = *(const __attribute__((address_space(3))) bf16x8*)(&As[a_row0 + 32 * i * GBK + koff[ks]]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int n = wn * 64 + 32 * j + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bt[n * GBK + 8 * swz_b(n, 2 * ks + g)]);
-      }
+      for (int j = 0; j < NT; ++j)
+        bfr[j] = *(const __attribute__((address_space(3))) bf16x8*)(&Bs[b_row0 + 32 * j * GBK + koff[ks]]);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)  // C^T tile: rows n, columns m
+        for (int j = 0; j < NT; ++j)  // C^T tile: rows n, columns m
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // epilogue inputs fetched up front so that their latency hides under the
+  // k loop: each lane's row records (f1) or residual values (f2), and the
+  // block's column sums (f1, into LDS)
+  __shared__ __attribute__((aligned(16))) float cs_lds[EPI == 0 ? BN : 4];
+  RowInfo rinfo[MT];
+  u32x2 resid[MT][NT][4];
+  if (EPI == 0) {
+    if (tid < BN / 4)
+      *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.colsum[n0 + 4 * tid]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) rinfo[i] = route.rows[min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          resid[i][j][q] = *reinterpret_cast<const u32x2*>(R + static_cast<int64_t>(m) * N + n0 + wn * (BN / 2) +
+                                                           32 * j + 8 * q + 4 * g);
     }
   }
 
-  if (EPI == 0) {
-    // column sums of this block's 128 columns of W, summed over the 16 row
-    // groups in a fixed order
-#pragma unroll
-    for (int j = 0; j < 8; ++j) colsum_part[(tid / 16) * GBN + 8 * (tid % 16) + j] = csum[j];
-    __syncthreads();
-    if (tid < GBN) {
-      float s = 0.f;
-      for (int q = 0; q < 16; ++q) s += colsum_part[q * GBN + tid];
-      colsum_part[tid] = s;  // row 0 is read only after the barrier below
-    }
-    __syncthreads();
+  const int nk = K / GBK;
+  copy_k(0, A0, B0);
+  __syncthreads();  // k step 0 in buffer 0
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 1 < nk) copy_k((kt + 1) * GBK, A1, B1);
+    __builtin_amdgcn_sched_barrier(0);  // issue the copy before this step's reads
+    mma_k(A0, B0);
+    __syncthreads();  // buffer 1 filled; buffer 0 free
+    if (kt + 1 >= nk) break;
+    if (kt + 2 < nk) copy_k((kt + 2) * GBK, A0, B0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_k(A1, B1);
+    __syncthreads();  // buffer 0 filled; buffer 1 free
   }
 
   // epilogue: lane owns row m = ... + l32 and columns n = ... + 8 (r/4) + 4 g + [0, 4)
@@ -170,26 +185,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     float mu = 0.f, rstd = 1.f;
     int64_t pool_row = -1;  // element offset of (page, head 0, slot) of row m, or -1
     if (EPI == 0) {
-      float2 st = route.stats[m];
-      mu = st.x;
-      rstd = st.y;
-      if (route.k_pool) {
-        const int user = find_segment(route.new_offsets, route.B, m);
-        const int pos = route.start_pos[user] + (m - route.new_offsets[user]);
-        const int lp = pos / route.page_size;
-        if (lp < route.max_pages) {
-          const int page = route.page_table[static_cast<int64_t>(user) * route.max_pages + lp];
-          if (page >= 0 && page < route.num_pages)
-            pool_row = route.pool_layer_offset +
-                       (static_cast<int64_t>(page) * route.H * route.page_size + (pos - lp * route.page_size)) *
-                           route.dh;
-        }
-      }
+      mu = rinfo[i].mean;
+      rstd = rinfo[i].rstd;
+      if (route.k_pool && rinfo[i].pool_row >= 0) pool_row = route.pool_layer_offset + rinfo[i].pool_row;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NT; ++j) {
       // 32 columns starting at a multiple of 32: one chunk, one head (uniform)
-      const int nb = n0 + wn * 64 + 32 * j;
+      const int nb = n0 + wn * (BN / 2) + 32 * j;
       const int chunk = EPI == 0 ? nb / route.inner : 0;  // 0 U, 1 V, 2 Q, 3 K
       const int cb = nb - chunk * route.inner;
       const int h = EPI == 0 ? cb / route.dh : 0;
@@ -200,20 +203,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       uint16_t* pool = chunk == 3 ? route.k_pool : route.v_pool;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nl = wn * 64 + 32 * j + 8 * q + 4 * g;  // local column of the 4-group
-        const int n = n0 + nl;
+        const int n = nb + 8 * q + 4 * g;  // first of this lane's 4 columns
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
         if (EPI == 0) {
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(&colsum_part[nl]);
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(&cs_lds[n - n0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = rstd * (v[e] - mu * cs[e]);
             v[e] = z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896340736f));
           }
         } else {
-          const u32x2 r2 = *reinterpret_cast<const u32x2*>(R + static_cast<int64_t>(m) * N + n);
+          const u32x2 r2 = resid[i][j][q];
           v[0] += bf2f(r2[0] & 0xFFFFu);
           v[1] += bf2f(r2[0] >> 16);
           v[2] += bf2f(r2[1] & 0xFFFFu);
@@ -235,17 +237,55 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   }
 }
 
-// per-row (mean, rstd) of x: one wave per row, two-pass from registers
+// Per-row (mean, rstd) of x: one wave per row, two-pass from registers.
+// Blocks past the rows' blocks sum the rows of Wt (the column sums of W1 that
+// the f1 epilogue needs), one wave per row.
 constexpr int kStatRows = 4;
 __global__ __launch_bounds__(64 * kStatRows) void row_stats_kernel(const uint16_t* __restrict__ x,
-                                                                   float2* __restrict__ stats,
+                                                                   RowInfo* __restrict__ info,
                                                                    int32_t rows, int32_t cols,
-                                                                   float eps) {
+                                                                   float eps,
+                                                                   const uint16_t* __restrict__ wt,
+                                                                   float* __restrict__ colsum,
+                                                                   int32_t wt_rows, RowPages pg) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kStatRows + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint16_t* xr = x + static_cast<int64_t>(row) * cols;
+  const int stat_blocks = (rows + kStatRows - 1) / kStatRows;
   constexpr int kMaxChunks = 4;  // cols <= 64 * 8 * 4
+  if (static_cast<int>(blockIdx.x) >= stat_blocks) {
+    const int n = (blockIdx.x - stat_blocks) * kStatRows + (threadIdx.x >> 6);
+    if (n >= wt_rows) return;
+    const uint16_t* wr = wt + static_cast<int64_t>(n) * cols;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int col = 8 * (lane + 64 * c);
+      if (col < cols) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(wr + col);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s += bf2f(static_cast<uint16_t>((e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu)));
+      }
+    }
+    s = wave_sum(s);
+    if (lane == 0) colsum[n] = s;
+    return;
+  }
+  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kStatRows + (threadIdx.x >> 6));
+  if (row >= rows) return;
+  // the page slot this new token's K/V rows go to (-1: none); the row is
+  // wave-uniform, so these are scalar loads that overlap the row's loads
+  int64_t pool_row = -1;
+  if (pg.page_table) {
+    const QBlock qb = pg.qblocks[pg.row_qblock[row]];
+    const int pos = qb.pos0 + (row - qb.row0);
+    const int lp = pos / pg.page_size;
+    if (lp < pg.max_pages) {
+      const int page = pg.page_table[static_cast<int64_t>(qb.user) * pg.max_pages + lp];
+      if (page >= 0 && page < pg.num_pages)
+        pool_row = (static_cast<int64_t>(page) * pg.H * pg.page_size + (pos - lp * pg.page_size)) * pg.dh;
+    }
+  }
+  const uint16_t* xr = x + static_cast<int64_t>(row) * cols;
   float v[kMaxChunks * 8];
   float s = 0.f;
 #pragma unroll
@@ -272,7 +312,7 @@ __global__ __launch_bounds__(64 * kStatRows) void row_stats_kernel(const uint16_
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) / cols + eps);
-  if (lane == 0) stats[row] = float2{mean, rstd};
+  if (lane == 0) info[row] = RowInfo{mean, rstd, pool_row};
 }
 
 constexpr int FT = 64, FK = 16;
@@ -295,7 +335,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       As[kk][mm] = (m < M && k < K) ? A[static_cast<int64_t>(m) * K + k] : 0.f;
       int nn = i % FT, kb = i / FT;
       int n = n0 + nn, k2 = k0 + kb;
-      Bs[kb][nn] = (n < N && k2 < K) ? Bm[static_cast<int64_t>(k2) * N + n] : 0.f;
+      Bs[kb][nn] = (n < N && k2 < K) ? Bm[static_cast<int64_t>(n) * K + k2] : 0.f;
     }
     __syncthreads();
     for (int kk = 0; kk < FK; ++kk)
@@ -318,41 +358,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_row_stats(const void* x, float* stats, int32_t rows, int32_t cols, float eps,
+hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
+                            const void* w1t, float* colsum, int32_t w1t_rows, const RowPages& pg,
                             hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (cols % 8 != 0 || cols > 64 * 8 * 4) return hipErrorInvalidValue;
-  dim3 grid((rows + kStatRows - 1) / kStatRows), block(64 * kStatRows);
-  hipLaunchKernelGGL(row_stats_kernel, grid, block, 0, s, static_cast<const uint16_t*>(x),
-                     reinterpret_cast<float2*>(stats), rows, cols, eps);
+  const int blocks = (rows + kStatRows - 1) / kStatRows + (w1t_rows + kStatRows - 1) / kStatRows;
+  hipLaunchKernelGGL(row_stats_kernel, dim3(blocks), dim3(64 * kStatRows), 0, s,
+                     static_cast<const uint16_t*>(x), info, rows, cols, eps,
+                     static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
   return hipGetLastError();
 }
 
-hipError_t launch_f1_bf16(const void* x, const float* stats, const void* w1, const F1Args& f,
-                          int32_t M, int32_t N, int32_t K, hipStream_t s) {
+template <int BM, int BN>
+static unsigned gemm_grid(int32_t M, int32_t N) {
+  const unsigned tiles = static_cast<unsigned>(((M + BM - 1) / BM) * (N / BN));
+  return (tiles + 7u) / 8u * 8u;  // a multiple of the 8 XCDs
+}
+
+hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
+                          const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (N % GBN != 0 || K % GBK != 0 || f.inner % 32 != 0 || f.dh % 32 != 0) return hipErrorInvalidValue;
+  constexpr int BM = 128, BN = 128;
+  if (N % BN != 0 || K % GBK != 0 || f.inner % 32 != 0 || f.dh % 32 != 0) return hipErrorInvalidValue;
   F1Route r{};
-  r.stats = reinterpret_cast<const float2*>(stats);
+  r.rows = info;
+  r.colsum = colsum;
   r.uvqk = static_cast<uint16_t*>(f.uvqk);
   r.inner = f.inner;
   r.kv_to_uvqk = f.kv_to_uvqk;
   r.k_pool = static_cast<uint16_t*>(f.k_pool);
   r.v_pool = static_cast<uint16_t*>(f.v_pool);
   r.pool_layer_offset = f.pool_layer_offset;
-  r.page_table = f.page_table;
-  r.new_offsets = f.new_offsets;
-  r.start_pos = f.start_pos;
-  r.B = f.B;
-  r.max_pages = f.max_pages;
-  r.num_pages = f.num_pages;
-  r.H = f.H;
   r.dh = f.dh;
   r.page_size = f.page_size;
-  constexpr int BM = 128;
-  dim3 grid(static_cast<unsigned>(((M + BM - 1) / BM) * (N / GBN)));
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, 0>), grid, dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1t),
                      static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
   return hipGetLastError();
 }
@@ -362,10 +403,9 @@ hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, v
   if (M == 0) return hipSuccess;
   if (dtype == HSTU_BF16) {
     // the bf16 path only uses this for f2 (+ residual); f1 goes through launch_f1_bf16
-    if (epilogue != 1 || N % GBN != 0 || K % GBK != 0) return hipErrorInvalidValue;
-    constexpr int BM = 64;  // a short K loop: more blocks hide more load latency
-    dim3 grid(static_cast<unsigned>(((M + BM - 1) / BM) * (N / GBN)));
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, 1>), grid, dim3(256), 0, s,
+    constexpr int BM = 64, BN = 128;
+    if (epilogue != 1 || N % BN != 0 || K % GBK != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
                        static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), F1Route{}, M, N,
                        K);

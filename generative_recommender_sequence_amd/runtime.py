@@ -42,15 +42,16 @@ def require_gpu():
 
 
 class Model:
-    """Device copies of a stack's weights: W1 [d][4*H*dh], W2 [H*dh][d] in the
-    compute dtype, rab [num_buckets] fp32, per layer."""
+    """Device copies of a stack's weights in the library's output-major layout
+    (w1 = W1^T [4*H*dh][d], w2 = W2^T [d][H*dh], for x . W1 and g . W2) in the
+    compute dtype, and rab [num_buckets] fp32, per layer."""
 
     def __init__(self, layers, dtype: int, num_heads: int, head_dim: int, d_model: int,
                  eps: float = 1e-5, device="cuda"):
         self.dtype, self.num_heads, self.head_dim, self.d_model, self.eps = dtype, num_heads, head_dim, d_model, eps
         t = tdtype(dtype)
-        self.w1 = [torch.from_numpy(np.ascontiguousarray(lw.w1)).to(device=device, dtype=t) for lw in layers]
-        self.w2 = [torch.from_numpy(np.ascontiguousarray(lw.w2)).to(device=device, dtype=t) for lw in layers]
+        self.w1 = [torch.from_numpy(np.ascontiguousarray(lw.w1.T)).to(device=device, dtype=t) for lw in layers]
+        self.w2 = [torch.from_numpy(np.ascontiguousarray(lw.w2.T)).to(device=device, dtype=t) for lw in layers]
         self.rab = [torch.from_numpy(np.ascontiguousarray(lw.rab, dtype=np.float32)).to(device) for lw in layers]
 
     @property

@@ -242,8 +242,11 @@ typedef struct {
   const hstu_plan *plan;    /* uploaded */
   const void *x;            /* device [n_new_total][d_model] */
   void *y;                  /* device [n_new_total][d_model], must not overlap x */
-  const void *w1;           /* device [d_model][4*H*head_dim] */
-  const void *w2;           /* device [H*head_dim][d_model] */
+  /* weights, output-major (row j holds the inputs' weights of output j):
+   * w1 [4*H*head_dim][d_model] is the transpose of the W1 in x . W1, w2
+   * [d_model][H*head_dim] the transpose of the W2 in g . W2 */
+  const void *w1;
+  const void *w2;
   const float *rab;         /* device fp32 [num_buckets] */
   int32_t num_buckets;
   /* paged (plan page_size > 0): K/V of the new tokens are appended to
