@@ -230,13 +230,21 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
       for (int32_t k = 0; k < np; ++k) {
         int32_t lo = static_cast<int32_t>(static_cast<int64_t>(nv) * k / np);
         int32_t hi = static_cast<int32_t>(static_cast<int64_t>(nv) * (k + 1) / np);
+        const QBlock& qb = p->qblocks[b];
+        const UserInfo& ui = p->users[qb.user];
         WorkItem w{};
-        w.user = p->qblocks[b].user;
+        w.user = qb.user;
         w.head = h;
         w.qblock = b;
         w.tile_begin = nv ? v[lo] : 0;
         w.tile_end = nv ? v[hi - 1] + 1 : 0;
         w.slot = slot++;
+        w.row0 = qb.row0;
+        w.count = qb.count;
+        w.pos0 = qb.pos0;
+        w.kv_len = ui.kv_len;
+        w.hist = ui.hist;
+        w.kv_row0 = ui.kv_row0;
         pieces.emplace_back(hi - lo, w);
       }
     }

@@ -29,9 +29,14 @@ constexpr int kMaxPos = 65535;
 
 // One attention work item: a block of up to kBlockQ queries of one user and
 // head, over the key tiles [tile_begin, tile_end) of that user.  Its result
-// (unnormalised sum over those keys) goes to partial slot `slot`.
+// (unnormalised sum over those keys) goes to partial slot `slot`.  It carries
+// the fields of its q-block and user that the kernels read, so that one
+// load brings everything.
 struct WorkItem {
-  int32_t user, head, qblock, tile_begin, tile_end, slot, pad0, pad1;
+  int32_t user, head, qblock, tile_begin, tile_end, slot;
+  int32_t row0, count, pos0;     // the q-block: first row, queries, first position
+  int32_t kv_len, hist, kv_row0;  // the user: keys, history length, first key row (contiguous)
+  int32_t pad[4];
 };
 
 // The partial slots of one (q-block, head): consecutive, in key order.

@@ -117,17 +117,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 
   const WorkItem w = a.plan.items[blockIdx.x];
   if (w.slot < 0) return;  // padding entry of the dispatch order
-  const QBlock qb = a.plan.qblocks[w.qblock];
-  const UserInfo ui = a.plan.users[w.user];
   const int h = w.head;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = uniform(tid >> 6);
   const int wq0 = wave * 32;                 // first local query of this wave
-  const bool wave_active = wq0 < qb.count;
+  const bool wave_active = wq0 < w.count;
   const int qlocal = wq0 + l32;
-  const int qpos = qb.pos0 + qlocal;         // sequence position of this lane's query
-  const int qa = qb.pos0, qe = qb.pos0 + qb.count;
-  const int hist = ui.hist;
+  const int qpos = w.pos0 + qlocal;          // sequence position of this lane's query
+  const int qa = w.pos0, qe = w.pos0 + w.count;
+  const int hist = w.hist;
   const int nb = a.num_buckets;
   const int vis_lim = min(qpos, hist);       // keys below this are visible; so is key == qpos
 
@@ -150,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   // Q^T as the B operand of S^T = K . Q^T: lane holds q[query l32][16 s + 8 g .. +8]
   bf16x8 qf[DH / 16];
   {
-    const bool qv = qlocal < qb.count;
-    const uint16_t* qrow = qbase + static_cast<int64_t>(qb.row0 + (qv ? qlocal : 0)) * a.q_stride + h * DH;
+    const bool qv = qlocal < w.count;
+    const uint16_t* qrow = qbase + static_cast<int64_t>(w.row0 + (qv ? qlocal : 0)) * a.q_stride + h * DH;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       u32x4 raw = qv ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
@@ -175,17 +173,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     loffk[i] = static_cast<int>(r * row_stride) + 8 * (lslot ^ kswz(r));
     loffv[i] = static_cast<int>(r * row_stride) + 8 * (lslot ^ vswz(r));
   }
-  auto copy_tile = [&](int tile, lds_u16* Kd, lds_u16* Vd) {
+  // page of logical page lp of this user: from the staged slice, or (for the
+  // first tile, copied before the slice is staged) from the table itself
+  auto page_lds = [&](int lp) { return pages_lds[lp - pg0]; };
+  auto page_glb = [&](int lp) {
+    return a.page_table[static_cast<int64_t>(w.user) * a.plan.max_pages + lp];
+  };
+  auto copy_tile = [&](int tile, lds_u16* Kd, lds_u16* Vd, auto&& page_of) {
     const int k0 = tile * KT;
     const int r0 = k0 + 16 * wave;  // first key of this wave's rows
-    if (r0 + 16 <= ui.kv_len) {
+    if (r0 + 16 <= w.kv_len) {
       int64_t base;
       if (PAGED) {
-        int page = uniform(pages_lds[(r0 >> p_shift) - pg0]);
+        int page = uniform(page_of(r0 >> p_shift));
         page = (page >= 0 && page < a.num_pages) ? page : 0;
         base = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (r0 & (P - 1))) * DH;
       } else {
-        base = static_cast<int64_t>(ui.kv_row0 + r0) * a.kv_stride + h * DH;
+        base = static_cast<int64_t>(w.kv_row0 + r0) * a.kv_stride + h * DH;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -198,28 +202,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + lrow;
-        const int key = min(r0 + r, ui.kv_len - 1);
+        const int key = min(r0 + r, w.kv_len - 1);
         int64_t off;
         if (PAGED) {
-          int page = pages_lds[(key >> p_shift) - pg0];
+          int page = page_of(key >> p_shift);
           page = (page >= 0 && page < a.num_pages) ? page : 0;
           off = a.pool_layer_offset + ((static_cast<int64_t>(page) * a.plan.H + h) * P + (key & (P - 1))) * DH;
         } else {
-          off = static_cast<int64_t>(ui.kv_row0 + key) * a.kv_stride + h * DH;
+          off = static_cast<int64_t>(w.kv_row0 + key) * a.kv_stride + h * DH;
         }
         dma16(kbase + off + 8 * (lslot ^ kswz(r)), Kd + (16 * wave + 4 * i) * DH);
         dma16(vbase + off + 8 * (lslot ^ vswz(r)), Vd + (16 * wave + 4 * i) * DH);
       }
     }
   };
-  auto fill_bias = [&](int tile, float* bias_rev) {
+  // bias table of a tile, from the staged rab (or, for the first tile, filled
+  // before rab is staged, from rab itself)
+  auto fill_bias = [&](int tile, float* bias_rev, bool from_global) {
     const int k0 = tile * KT;
     if (needs_bias_table(k0, qa, qe, hist, nb) && tid < kBiasLen) {
       const int d = qa + BQ - 1 - k0 - tid;
-      bias_rev[tid] = d < 0 ? 0.f : rab_s[rel_bucket(d, nb)];
+      const int bk = rel_bucket(d, nb);
+      bias_rev[tid] = d < 0 ? 0.f : (from_global ? a.rab[bk] * kLog2e : rab_s[bk]);
     }
   };
-
   // per-lane LDS read offsets (elements), hoisted out of the tile loop
   int kaddr[DH / 16];  // A operand of S^T: row vperm(l32) (+32 per row block), chunk (2s+g)
   {
@@ -318,21 +324,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     while (t < w.tile_end && !visible_tile(t)) ++t;
     return t;
   };
+  // the first tile's copy and bias go out with the rest of the set-up loads
   int t = w.tile_begin;
   while (t < w.tile_end && !visible_tile(t)) ++t;
-  __syncthreads();  // rab and page-table slice staged
   if (t < w.tile_end) {
-    fill_bias(t, bias0);
-    copy_tile(t, K0, V0);
+    fill_bias(t, bias0, true);
+    copy_tile(t, K0, V0, page_glb);
   }
-  __syncthreads();  // tile t in buffer 0
+  __syncthreads();  // rab, page-table slice and tile t staged
 
   // two tiles per trip so that each half names its buffers statically
   while (t < w.tile_end) {
     int tn = next_visible(t);
     if (tn < w.tile_end) {
-      fill_bias(tn, bias1);
-      copy_tile(tn, K1, V1);
+      fill_bias(tn, bias1, false);
+      copy_tile(tn, K1, V1, page_lds);
     }
     __builtin_amdgcn_sched_barrier(0);  // issue the copy before the tile's LDS reads
     if (wave_active) compute_tile(t, K0, V0, bias0);
@@ -341,8 +347,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     t = tn;
     tn = next_visible(t);
     if (tn < w.tile_end) {
-      fill_bias(tn, bias0);
-      copy_tile(tn, K0, V0);
+      fill_bias(tn, bias0, false);
+      copy_tile(tn, K0, V0, page_lds);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (wave_active) compute_tile(t, K1, V1, bias1);
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       int row = wq0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (row < qb.count) out[row * DH + 32 * nt + l32] = oacc[nt][r];
+      if (row < w.count) out[row * DH + 32 * nt + l32] = oacc[nt][r];
     }
 }
 
@@ -373,22 +379,20 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
   __shared__ float Vs[SK][D + 1];
   const WorkItem w = a.plan.items[blockIdx.x];
   if (w.slot < 0) return;  // padding entry of the dispatch order
-  const QBlock qb = a.plan.qblocks[w.qblock];
-  const UserInfo ui = a.plan.users[w.user];
   const int h = w.head, tid = threadIdx.x;
-  const int qpos = qb.pos0 + tid;
-  const bool qv = tid < qb.count;
+  const int qpos = w.pos0 + tid;
+  const bool qv = tid < w.count;
   const float* qbase = static_cast<const float*>(a.q);
   const float* kbase = static_cast<const float*>(PAGED ? a.k_pool : a.k);
   const float* vbase = static_cast<const float*>(PAGED ? a.v_pool : a.v);
   float q[D], o[D];
   for (int e = 0; e < D; ++e) {
-    q[e] = qv ? qbase[static_cast<int64_t>(qb.row0 + tid) * a.q_stride + h * D + e] : 0.f;
+    q[e] = qv ? qbase[static_cast<int64_t>(w.row0 + tid) * a.q_stride + h * D + e] : 0.f;
     o[e] = 0.f;
   }
-  const int qa = qb.pos0, qe = qb.pos0 + qb.count;
+  const int qa = w.pos0, qe = w.pos0 + w.count;
   for (int tile = w.tile_begin; tile < w.tile_end; ++tile) {
-    if (!tile_visible_dev(tile * KT, qa, qe, ui.hist)) continue;
+    if (!tile_visible_dev(tile * KT, qa, qe, w.hist)) continue;
     for (int sub = 0; sub < KT; sub += SK) {
       const int k0 = tile * KT + sub;
       __syncthreads();
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
         int kk = i / D, e = i % D, j = k0 + kk;
         const float* kr = nullptr;
         const float* vr = nullptr;
-        if (j < ui.kv_len) {
+        if (j < w.kv_len) {
           if (PAGED) {
             const int P = a.plan.page_size;
             int lp = j / P;
@@ -410,8 +414,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
               vr = vbase + off;
             }
           } else {
-            kr = kbase + static_cast<int64_t>(ui.kv_row0 + j) * a.kv_stride + h * D;
-            vr = vbase + static_cast<int64_t>(ui.kv_row0 + j) * a.kv_stride + h * D;
+            kr = kbase + static_cast<int64_t>(w.kv_row0 + j) * a.kv_stride + h * D;
+            vr = vbase + static_cast<int64_t>(w.kv_row0 + j) * a.kv_stride + h * D;
           }
         }
         Ks[kk][e] = kr ? kr[e] : 0.f;
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
       if (!qv) continue;
       for (int kk = 0; kk < SK; ++kk) {
         const int j = k0 + kk;
-        const bool vis = (j == qpos) || (j < qpos && j < ui.hist);
+        const bool vis = (j == qpos) || (j < qpos && j < w.hist);
         if (!vis) continue;
         float s = 0.f;
         for (int e = 0; e < D; ++e) s += q[e] * Ks[kk][e];
