@@ -83,34 +83,62 @@ StagingRing& staging() {
 
 }  // namespace
 
-hstu_status staged_upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  if (bytes == 0) return HSTU_OK;
-  StagingRing& r = staging();
-  std::lock_guard<std::mutex> lk(r.mu);
+namespace {
+// Takes the next slot of the ring (waiting for its previous use), sized for
+// `bytes`, and fills it from src.  Caller holds the ring's lock.
+hstu_status fill_slot(StagingRing& r, const void* src, size_t bytes, StagingRing::Slot** out) {
   StagingRing::Slot& sl = r.slots[r.next];
   r.next = (r.next + 1) % 4;
   hstu_status st;
   if (sl.pending) {
-    if ((st = check_hip(hipEventSynchronize(sl.done), "staged upload")) != HSTU_OK) return st;
+    if ((st = check_hip(hipEventSynchronize(sl.done), "staging")) != HSTU_OK) return st;
     sl.pending = false;
   }
-  if (!sl.done && (st = check_hip(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming), "staged upload")) != HSTU_OK)
+  if (!sl.done && (st = check_hip(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming), "staging")) != HSTU_OK)
     return st;
   if (sl.cap < bytes) {
-    if (sl.host && (st = check_hip(hipHostFree(sl.host), "staged upload")) != HSTU_OK) return st;
+    if (sl.host && (st = check_hip(hipHostFree(sl.host), "staging")) != HSTU_OK) return st;
     sl.host = nullptr;
     sl.cap = 0;
     size_t want = std::max(bytes, static_cast<size_t>(1) << 20);
-    if ((st = check_hip(hipHostMalloc(&sl.host, want, hipHostMallocDefault), "staged upload")) != HSTU_OK)
+    if ((st = check_hip(hipHostMalloc(&sl.host, want, hipHostMallocDefault), "staging")) != HSTU_OK)
       return st;
     sl.cap = want;
   }
   std::memcpy(sl.host, src, bytes);
-  if ((st = check_hip(hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream), "staged upload")) !=
+  *out = &sl;
+  return HSTU_OK;
+}
+}  // namespace
+
+hstu_status staged_upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return HSTU_OK;
+  StagingRing& r = staging();
+  std::lock_guard<std::mutex> lk(r.mu);
+  StagingRing::Slot* sl = nullptr;
+  hstu_status st;
+  if ((st = fill_slot(r, src, bytes, &sl)) != HSTU_OK) return st;
+  if ((st = check_hip(hipMemcpyAsync(dst, sl->host, bytes, hipMemcpyHostToDevice, stream), "staged upload")) !=
       HSTU_OK)
     return st;
-  if ((st = check_hip(hipEventRecord(sl.done, stream), "staged upload")) != HSTU_OK) return st;
-  sl.pending = true;
+  if ((st = check_hip(hipEventRecord(sl->done, stream), "staged upload")) != HSTU_OK) return st;
+  sl->pending = true;
+  return HSTU_OK;
+}
+
+hstu_status staged_host(const void* src, size_t bytes, hipStream_t stream,
+                        hipError_t (*use)(const void* slot, void* ctx), void* ctx) {
+  if (bytes == 0) return HSTU_OK;
+  StagingRing& r = staging();
+  std::lock_guard<std::mutex> lk(r.mu);
+  StagingRing::Slot* sl = nullptr;
+  hstu_status st;
+  if ((st = fill_slot(r, src, bytes, &sl)) != HSTU_OK) return st;
+  void* dev = nullptr;
+  if ((st = check_hip(hipHostGetDevicePointer(&dev, sl->host, 0), "staging")) != HSTU_OK) return st;
+  if ((st = check_hip(use(dev, ctx), "staged launch")) != HSTU_OK) return st;
+  if ((st = check_hip(hipEventRecord(sl->done, stream), "staging")) != HSTU_OK) return st;
+  sl->pending = true;
   return HSTU_OK;
 }
 

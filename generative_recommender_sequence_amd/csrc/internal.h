@@ -104,7 +104,13 @@ struct hstu_kv_cache {
   void* v_pool = nullptr;
   int64_t tick = 0;
   std::deque<int32_t> free_q;
-  std::unordered_map<int64_t, User> users;
+  std::unordered_map<int64_t, User> users;  // device-resident users
+  // host tier (host_pages < 0: none attached)
+  int32_t host_pages = -1;
+  void* host_k = nullptr;  // device-visible addresses of the caller's pinned host pools
+  void* host_v = nullptr;
+  std::deque<int32_t> host_free_q;
+  std::unordered_map<int64_t, User> host_users;
 };
 
 namespace hstu {
@@ -129,6 +135,20 @@ hipError_t launch_append(int dtype, const PlanDev* plan_or_null, int32_t B,
                          const void* v_new, int64_t row_stride, int32_t n_new_total, void* k_pool,
                          void* v_pool, int32_t layer, int32_t num_pages, int32_t H, int32_t dh,
                          int32_t page_size, hipStream_t s);
+// Copies whole pages (all heads) of every layer, K and V, between two pools:
+// pairs (host pinned, device-visible) [n_pairs] of (source page, destination
+// page); each pool is [layers][pages][page_bytes].
+struct PagePair {
+  int32_t src, dst;
+};
+hipError_t launch_tier_copy(const PagePair* pairs, int32_t n_pairs, int32_t layers, const void* src_k,
+                            const void* src_v, int64_t src_pages, void* dst_k, void* dst_v,
+                            int64_t dst_pages, int64_t page_bytes, hipStream_t s);
+// Copies `bytes` of src into a pinned staging slot and calls use(slot) with
+// the slot's (device-visible) address; the slot is reused only after the work
+// `use` enqueued on `stream` has finished.
+hstu_status staged_host(const void* src, size_t bytes, hipStream_t stream,
+                        hipError_t (*use)(const void* slot, void* ctx), void* ctx);
 hipError_t launch_gather(int dtype, int32_t B, const int32_t* d_page_table, int32_t max_pages,
                          const int32_t* d_kv_len, const int32_t* d_out_offsets, int32_t n_out_total,
                          void* k_out, void* v_out, const void* k_pool, const void* v_pool,

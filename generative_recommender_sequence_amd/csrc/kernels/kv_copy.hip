@@ -111,4 +111,35 @@ hipError_t launch_gather(int dtype, int32_t B, const int32_t* d_page_table, int3
   return hipGetLastError();
 }
 
+namespace {
+// One block per (page pair, layer, K or V): a whole page of all heads, 16
+// bytes per lane per step.
+__global__ __launch_bounds__(256) void tier_copy_kernel(const PagePair* __restrict__ pairs, int32_t layers,
+                                                       const u32x4* __restrict__ sk, const u32x4* __restrict__ sv,
+                                                       int64_t src_pages, u32x4* __restrict__ dk,
+                                                       u32x4* __restrict__ dv, int64_t dst_pages,
+                                                       int64_t page_chunks) {
+  int64_t idx = blockIdx.x;
+  const int kv = static_cast<int>(idx & 1);
+  idx >>= 1;
+  const int64_t layer = idx % layers;
+  const PagePair pp = pairs[idx / layers];
+  const u32x4* src = (kv ? sv : sk) + (layer * src_pages + pp.src) * page_chunks;
+  u32x4* dst = (kv ? dv : dk) + (layer * dst_pages + pp.dst) * page_chunks;
+  for (int64_t i = threadIdx.x; i < page_chunks; i += blockDim.x) dst[i] = src[i];
+}
+}  // namespace
+
+hipError_t launch_tier_copy(const PagePair* pairs, int32_t n_pairs, int32_t layers, const void* src_k,
+                            const void* src_v, int64_t src_pages, void* dst_k, void* dst_v,
+                            int64_t dst_pages, int64_t page_bytes, hipStream_t s) {
+  if (n_pairs == 0 || layers == 0) return hipSuccess;
+  if (page_bytes % 16 != 0) return hipErrorInvalidValue;
+  const int64_t blocks = static_cast<int64_t>(n_pairs) * layers * 2;
+  hipLaunchKernelGGL(tier_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pairs, layers,
+                     static_cast<const u32x4*>(src_k), static_cast<const u32x4*>(src_v), src_pages,
+                     static_cast<u32x4*>(dst_k), static_cast<u32x4*>(dst_v), dst_pages, page_bytes / 16);
+  return hipGetLastError();
+}
+
 }  // namespace hstu

@@ -69,12 +69,17 @@ SIGNATURES = {
     "kv_cache_destroy": (c_i32, [c_vp]),
     "kv_lookup": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "kv_evict_lru": (c_i32, [c_vp, c_i32, P_i64, c_i32, P_i64, c_i32, P_i32]),
+    "kv_lru_victims": (c_i32, [c_vp, c_i32, P_i64, c_i32, P_i64, c_i32, P_i32]),
     "kv_page_alloc": (c_i32, [c_vp, P_i64, P_i32, c_i32, P_i32, c_i32, P_i32]),
     "kv_truncate": (c_i32, [c_vp, c_i64, c_i32]),
     "kv_free_pages": (c_i32, [c_vp, P_i32]),
     "kv_page_table": (c_i32, [c_vp, P_i64, c_i32, P_i32, c_i32, P_i32]),
     "kv_state_dump": (c_i32, [c_vp, c_vp, c_size, ctypes.POINTER(c_size)]),
     "kv_state_load": (c_i32, [c_vp, c_vp, c_size]),
+    "kv_host_attach": (c_i32, [c_vp, c_vp, c_vp, c_i32]),
+    "kv_residency": (c_i32, [c_vp, P_i64, c_i32, P_i32, P_i32]),
+    "kv_offload": (c_i32, [c_vp, P_i64, c_i32, P_i64, c_i32, c_vp, P_i64, c_i32, P_i32]),
+    "kv_onboard": (c_i32, [c_vp, P_i64, c_i32, c_vp]),
     "kv_page_append": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32, c_vp]),
     "kv_page_gather": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "hstu_plan_create": (c_i32, [ctypes.POINTER(hstu_batch_desc), ctypes.POINTER(c_vp)]),
@@ -157,6 +162,15 @@ def kv_evict_lru(h: int, pages_needed: int, pinned, cap: int = 1 << 16) -> np.nd
     return ev[:n.value].copy()
 
 
+def kv_lru_victims(h: int, pages_needed: int, pinned, cap: int = 1 << 16) -> np.ndarray:
+    p = _arr(pinned, np.int64) if len(pinned) else np.zeros(1, np.int64)
+    ev = np.zeros(max(cap, 1), np.int64)
+    n = c_i32(0)
+    _check(lib().kv_lru_victims(h, int(pages_needed), _ptr(p, c_i64), len(pinned), _ptr(ev, c_i64), cap,
+                                ctypes.byref(n)), "kv_lru_victims")
+    return ev[:n.value].copy()
+
+
 def kv_page_alloc(h: int, users, n_new, max_pages: int):
     u = _arr(users, np.int64)
     nn = _arr(n_new, np.int32)
@@ -197,6 +211,35 @@ def kv_state_dump(h: int) -> bytes:
 def kv_state_load(h: int, data: bytes):
     buf = (ctypes.c_uint8 * max(len(data), 1)).from_buffer_copy(data if data else b"\0")
     _check(lib().kv_state_load(h, buf, len(data)), "kv_state_load")
+
+
+def kv_host_attach(h: int, host_pages: int, host_k_pool: int = 0, host_v_pool: int = 0):
+    _check(lib().kv_host_attach(h, host_k_pool or None, host_v_pool or None, int(host_pages)),
+           "kv_host_attach")
+
+
+def kv_residency(h: int, users):
+    u = _arr(users, np.int64)
+    where = np.zeros(max(len(u), 1), np.int32)
+    ln = np.zeros(max(len(u), 1), np.int32)
+    _check(lib().kv_residency(h, _ptr(u, c_i64), len(u), _ptr(where, c_i32), _ptr(ln, c_i32)),
+           "kv_residency")
+    return where[:len(u)].copy(), ln[:len(u)].copy()
+
+
+def kv_offload(h: int, users, stream: int = 0, pinned=(), cap: int = 1 << 16) -> np.ndarray:
+    u = _arr(users, np.int64) if len(users) else np.zeros(1, np.int64)
+    p = _arr(pinned, np.int64) if len(pinned) else np.zeros(1, np.int64)
+    ev = np.zeros(max(cap, 1), np.int64)
+    n = c_i32(0)
+    _check(lib().kv_offload(h, _ptr(u, c_i64), len(users), _ptr(p, c_i64), len(pinned), stream or None,
+                            _ptr(ev, c_i64), cap, ctypes.byref(n)), "kv_offload")
+    return ev[:n.value].copy()
+
+
+def kv_onboard(h: int, users, stream: int = 0):
+    u = _arr(users, np.int64) if len(users) else np.zeros(1, np.int64)
+    _check(lib().kv_onboard(h, _ptr(u, c_i64), len(users), stream or None), "kv_onboard")
 
 
 def kv_page_append(h: int, layer: int, B: int, d_new_offsets: int, d_start_pos: int, d_page_table: int,
@@ -241,6 +284,12 @@ class KVCache:
         except HstuError as e:
             return e.status, []
 
+    def lru_victims(self, pages_needed, pinned, cap=1 << 16):
+        try:
+            return HSTU_OK, kv_lru_victims(self.h, pages_needed, pinned, cap)
+        except HstuError as e:
+            return e.status, []
+
     def alloc(self, users, n_new, max_pages):
         try:
             pt, kl = kv_page_alloc(self.h, users, n_new, max_pages)
@@ -251,6 +300,33 @@ class KVCache:
     def truncate(self, user, new_len):
         try:
             kv_truncate(self.h, user, new_len)
+            return HSTU_OK
+        except HstuError as e:
+            return e.status
+
+    def host_attach(self, host_pages, host_k_pool: int = 0, host_v_pool: int = 0):
+        try:
+            kv_host_attach(self.h, host_pages, host_k_pool, host_v_pool)
+            return HSTU_OK
+        except HstuError as e:
+            return e.status
+
+    def residency(self, users):
+        try:
+            where, ln = kv_residency(self.h, users)
+            return HSTU_OK, [int(x) for x in where], [int(x) for x in ln]
+        except HstuError as e:
+            return e.status, None, None
+
+    def offload(self, users, pinned=(), cap=1 << 16, stream: int = 0):
+        try:
+            return HSTU_OK, kv_offload(self.h, users, stream, pinned, cap)
+        except HstuError as e:
+            return e.status, []
+
+    def onboard(self, users, stream: int = 0):
+        try:
+            kv_onboard(self.h, users, stream)
             return HSTU_OK
         except HstuError as e:
             return e.status

@@ -73,6 +73,18 @@ class PagedCache:
         self.page_size, self.num_pages, self.dtype = page_size, num_pages, dtype
         self.h = hstu.kv_cache_create(num_layers, num_heads, head_dim, page_size, num_pages, dtype,
                                       self.k_pool.data_ptr(), self.v_pool.data_ptr(), free_order)
+        self.host_pages = 0
+        self.host_k = self.host_v = None
+
+    def attach_host(self, host_pages: int):
+        """A host tier of host_pages pages of the same geometry, its pools in
+        pinned host memory; users evicted for room are then offloaded to it
+        and onboarded again when they are requested."""
+        n = self.num_layers * host_pages * self.num_heads * self.page_size * self.head_dim
+        self.host_k = torch.zeros(max(n, 1), dtype=tdtype(self.dtype), pin_memory=True)
+        self.host_v = torch.zeros(max(n, 1), dtype=tdtype(self.dtype), pin_memory=True)
+        hstu.kv_host_attach(self.h, host_pages, self.host_k.data_ptr(), self.host_v.data_ptr())
+        self.host_pages = host_pages
 
     def __del__(self):
         if getattr(self, "h", None):
@@ -100,6 +112,9 @@ class Request:
     evicted: np.ndarray
     num_heads: int = 1
     head_dim: int = 128
+    offloaded: np.ndarray = None      # users moved to the host tier to make room
+    host_dropped: np.ndarray = None   # host-tier users dropped to make room there
+    onboarded: np.ndarray = None      # requested users brought back from the host tier
 
     def close(self):
         if self.plan:
@@ -147,17 +162,39 @@ def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None,
             bufs: Optional[RequestBuffers] = None) -> Request:
     """Host cache operations (lookup, LRU eviction, allocation), page-table
     upload, and the request plan, uploaded (asynchronously when `bufs` is
-    given)."""
+    given).  With a host tier, requested users found there are onboarded
+    (their cached length counts as a hit), and the LRU victims that make room
+    are offloaded to it rather than dropped (dropped only if the host tier
+    cannot take them); the page copies go on the request's stream."""
     users = np.asarray(users, np.int64)
     new_len = np.asarray(new_len, np.int32)
     n_targets = np.asarray(n_targets, np.int32)
     s = stream_handle(stream)
-    evicted = np.zeros(0, np.int64)
+    evicted = offloaded = host_dropped = onboarded = np.zeros(0, np.int64)
     if cache is not None:
         cached = hstu.kv_lookup(cache.h, users)
         need = cache.pages_needed(cached, new_len)
+        if cache.host_pages:
+            where, host_len = hstu.kv_residency(cache.h, users)
+            on_host = where == 2
+            onboarded = users[on_host]
+            cached = np.where(on_host, host_len, cached).astype(np.int32)
+            need = cache.pages_needed(cached, new_len) + sum(_ceil(c, cache.page_size) for c in cached[on_host])
         if hstu.kv_free_pages(cache.h) < need:
-            evicted = hstu.kv_evict_lru(cache.h, need, users)
+            if cache.host_pages:
+                # the step after choosing LRU victims: keep their pages on the host tier
+                victims = hstu.kv_lru_victims(cache.h, need, users)
+                try:
+                    host_dropped = hstu.kv_offload(cache.h, victims, s, pinned=onboarded)
+                    offloaded = victims
+                except hstu.HstuError as e:
+                    if e.status != hstu.HSTU_ERR_NO_SPACE:
+                        raise
+                    evicted = hstu.kv_evict_lru(cache.h, need, users)
+            else:
+                evicted = hstu.kv_evict_lru(cache.h, need, users)
+        if len(onboarded):
+            hstu.kv_onboard(cache.h, onboarded, s)
         pt, kv_len = hstu.kv_page_alloc(cache.h, users, new_len, max_pages)
         d_pt = bufs.upload_page_table(pt) if bufs is not None else torch.from_numpy(pt).to(device)
         page_size, num_heads, head_dim = cache.page_size, cache.num_heads, cache.head_dim
@@ -174,7 +211,8 @@ def prepare(cache: Optional[PagedCache], users, new_len, n_targets, norm_n=None,
         meta = torch.empty(max(int(info.meta_bytes), 256), dtype=torch.uint8, device=device)
     hstu.hstu_plan_upload(plan, meta.data_ptr(), meta.numel(), s)
     return Request(users, new_len, np.asarray(cached, np.int32), n_targets, nn, np.asarray(kv_len, np.int32),
-                   plan, info, meta, d_pt, max_pages, evicted, num_heads, head_dim)
+                   plan, info, meta, d_pt, max_pages, evicted, num_heads, head_dim, offloaded, host_dropped,
+                   onboarded)
 
 
 def layer_args(model: Model, req: Request, li: int, x: torch.Tensor, y: torch.Tensor,

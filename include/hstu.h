@@ -110,6 +110,12 @@ hstu_status kv_lookup(hstu_kv_cache *cache, const int64_t *users, int32_t B, int
 hstu_status kv_evict_lru(hstu_kv_cache *cache, int32_t pages_needed, const int64_t *pinned,
                          int32_t n_pinned, int64_t *evicted, int32_t cap, int32_t *n_evicted);
 
+/* The users kv_evict_lru would evict for the same arguments (victims, host
+ * out [cap], *n_victims), same errors, but nothing changes: with a host tier
+ * attached they are offloaded (kv_offload) instead of dropped. */
+hstu_status kv_lru_victims(const hstu_kv_cache *cache, int32_t pages_needed, const int64_t *pinned,
+                           int32_t n_pinned, int64_t *victims, int32_t cap, int32_t *n_victims);
+
 /* allocation [DT]: reserves room for n_new[b] (host [B]) more positions of
  * users[b] (host [B], distinct; a user not yet cached is created).  Pages
  * come from the head of the free queue, users in batch order; a user's last
@@ -133,14 +139,57 @@ hstu_status kv_free_pages(const hstu_kv_cache *cache, int32_t *n_free);
 hstu_status kv_page_table(const hstu_kv_cache *cache, const int64_t *users, int32_t B,
                           int32_t *page_table, int32_t max_pages, int32_t *kv_len);
 
-/* Canonical state bytes (little endian): u32 0x564B5348, u32 1, i32 num_pages,
- * i32 page_size, i64 tick, i32 n_users, i32 n_free; per user in ascending id:
- * i64 id, i32 len, i64 tick, i32 n_pages, i32 pages[n_pages]; then i32
- * free[n_free] from head to tail.  *needed = size; writes only if cap >= size. */
+/* Canonical state bytes (little endian): u32 0x564B5348, u32 version (1, or
+ * 2 with a host tier attached), i32 num_pages, i32 page_size, i64 tick, i32
+ * n_users, i32 n_free; per device-resident user in ascending id: i64 id, i32
+ * len, i64 tick, i32 n_pages, i32 pages[n_pages]; then i32 free[n_free] from
+ * head to tail.  Version 2 continues with i32 host_pages, i32 n_host_users,
+ * i32 n_host_free, the host-resident users in the same form, and the host
+ * free queue.  *needed = size; writes only if cap >= size. */
 hstu_status kv_state_dump(const hstu_kv_cache *cache, void *buf, size_t cap, size_t *needed);
 /* Replaces the metadata with a dump of a cache of the same geometry (the
  * pools are untouched).  INVALID (nothing changed) if inconsistent. */
 hstu_status kv_state_load(hstu_kv_cache *cache, const void *buf, size_t len);
+
+/* ---- host tier [DT: the KV data table spans GPU and host storage; users are
+ * onboarded from and offloaded to it] ---- */
+
+/* Attaches a host tier of host_pages pages of the same geometry: pools in
+ * caller-owned pinned host memory (hipHostMalloc), each
+ * [num_layers][host_pages][num_heads][page_size][head_dim], or both NULL for a
+ * metadata-only cache.  Its free queue starts as 0, 1, 2, ...  Once per cache
+ * (INVALID otherwise). */
+hstu_status kv_host_attach(hstu_kv_cache *cache, void *host_k_pool, void *host_v_pool, int32_t host_pages);
+
+/* where[b] (host out) = 0 absent, 1 on the device, 2 on the host tier; len[b]
+ * its length (0 if absent).  Ticks unchanged. */
+hstu_status kv_residency(const hstu_kv_cache *cache, const int64_t *users, int32_t B, int32_t *where,
+                         int32_t *len);
+
+/* offload [DT]: moves device-resident users (host [n], distinct) to the host
+ * tier.  If the host free queue is short, host-resident users not listed in
+ * pinned (host [n_pinned]) are dropped in ascending (tick, id) order (their
+ * pages join the host queue's tail in logical order; their ids go to
+ * host_evicted [cap], in drop order).  Then, users in order, each takes its
+ * host pages from the host queue's head, copies of every layer's K and V
+ * pages to them are enqueued on `stream`, and its device pages join the
+ * device free queue's tail in logical order; length and tick are kept.  Work
+ * enqueued later on `stream` may reuse the freed device pages; work on other
+ * streams must wait for it.  All-or-nothing: UNKNOWN_USER if one is not on
+ * the device, NO_SPACE if the host tier cannot hold them, INVALID if cap is
+ * too small. */
+hstu_status kv_offload(hstu_kv_cache *cache, const int64_t *users, int32_t n, const int64_t *pinned,
+                       int32_t n_pinned, hipStream_t stream, int64_t *host_evicted, int32_t cap,
+                       int32_t *n_host_evicted);
+
+/* onboard [DT]: moves host-resident users (host [n], distinct) back to the
+ * device: users in order, each takes its device pages from the device free
+ * queue's head, copies are enqueued on `stream`, its host pages join the host
+ * queue's tail in logical order, and it gets a fresh tick.  No eviction
+ * here (evict first).  All-or-nothing: UNKNOWN_USER if one is not on the
+ * host tier, NO_SPACE if free device pages are short.  A host-resident user
+ * counts as absent for kv_lookup and cannot be allocated until onboarded. */
+hstu_status kv_onboard(hstu_kv_cache *cache, const int64_t *users, int32_t n, hipStream_t stream);
 
 /* append [DT]: copies the K and V rows of the new tokens into their pages of
  * `layer`.  User b's new rows are d_new_offsets[b] .. d_new_offsets[b+1]-1

@@ -86,12 +86,23 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     lib.oracle_kv_lookup.argtypes = [vp, i64p, ctypes.c_int32, i32p]
     lib.oracle_kv_evict_lru.restype = ctypes.c_int
     lib.oracle_kv_evict_lru.argtypes = [vp, ctypes.c_int32, i64p, ctypes.c_int32, i64p, ctypes.c_int32, i32p]
+    lib.oracle_kv_lru_victims.restype = ctypes.c_int
+    lib.oracle_kv_lru_victims.argtypes = [vp, ctypes.c_int32, i64p, ctypes.c_int32, i64p, ctypes.c_int32, i32p]
     lib.oracle_kv_alloc.restype = ctypes.c_int
     lib.oracle_kv_alloc.argtypes = [vp, i64p, i32p, ctypes.c_int32, i32p, ctypes.c_int32, i32p]
     lib.oracle_kv_truncate.restype = ctypes.c_int
     lib.oracle_kv_truncate.argtypes = [vp, ctypes.c_int64, ctypes.c_int32]
     lib.oracle_kv_dump.restype = ctypes.c_int64
     lib.oracle_kv_dump.argtypes = [vp, ctypes.c_void_p, ctypes.c_int64]
+    lib.oracle_kv_host_attach.restype = ctypes.c_int
+    lib.oracle_kv_host_attach.argtypes = [vp, ctypes.c_int32]
+    lib.oracle_kv_residency.restype = ctypes.c_int
+    lib.oracle_kv_residency.argtypes = [vp, i64p, ctypes.c_int32, i32p, i32p]
+    lib.oracle_kv_offload.restype = ctypes.c_int
+    lib.oracle_kv_offload.argtypes = [vp, i64p, ctypes.c_int32, i64p, ctypes.c_int32, i64p, ctypes.c_int32,
+                                      i32p]
+    lib.oracle_kv_onboard.restype = ctypes.c_int
+    lib.oracle_kv_onboard.argtypes = [vp, i64p, ctypes.c_int32]
     _LIBS[mutant] = lib
     return lib
 
@@ -303,6 +314,14 @@ class KVOracle:
                                           _p(ev, ctypes.c_int64), cap, ctypes.byref(n))
         return rc, ev[:n.value].copy()
 
+    def lru_victims(self, pages_needed, pinned, cap=1 << 16):
+        p = _i64(pinned) if len(pinned) else np.zeros(1, np.int64)
+        ev = np.zeros(max(cap, 1), np.int64)
+        n = ctypes.c_int32(0)
+        rc = self.lib.oracle_kv_lru_victims(self.h, int(pages_needed), _p(p, ctypes.c_int64), len(pinned),
+                                            _p(ev, ctypes.c_int64), cap, ctypes.byref(n))
+        return rc, ev[:n.value].copy()
+
     def alloc(self, users, n_new, max_pages):
         u = _i64(users)
         nn = np.ascontiguousarray(n_new, dtype=np.int32)
@@ -321,6 +340,31 @@ class KVOracle:
         n2 = self.lib.oracle_kv_dump(self.h, buf, n)
         assert n2 == n
         return bytes(buf)
+
+    # host tier
+    def host_attach(self, host_pages):
+        return self.lib.oracle_kv_host_attach(self.h, int(host_pages))
+
+    def residency(self, users):
+        u = _i64(users) if len(users) else np.zeros(1, np.int64)
+        where = np.zeros(max(len(users), 1), np.int32)
+        ln = np.zeros(max(len(users), 1), np.int32)
+        rc = self.lib.oracle_kv_residency(self.h, _p(u, ctypes.c_int64), len(users), _p(where, ctypes.c_int32),
+                                          _p(ln, ctypes.c_int32))
+        return rc, where[:len(users)].copy(), ln[:len(users)].copy()
+
+    def offload(self, users, pinned=(), cap=1 << 16):
+        u = _i64(users) if len(users) else np.zeros(1, np.int64)
+        p = _i64(pinned) if len(pinned) else np.zeros(1, np.int64)
+        dr = np.zeros(max(cap, 1), np.int64)
+        n = ctypes.c_int32(0)
+        rc = self.lib.oracle_kv_offload(self.h, _p(u, ctypes.c_int64), len(users), _p(p, ctypes.c_int64),
+                                        len(pinned), _p(dr, ctypes.c_int64), cap, ctypes.byref(n))
+        return rc, dr[:n.value].copy()
+
+    def onboard(self, users):
+        u = _i64(users) if len(users) else np.zeros(1, np.int64)
+        return self.lib.oracle_kv_onboard(self.h, _p(u, ctypes.c_int64), len(users))
 
 
 def pool_offset(layer_idx, page, head, slot, num_pages, num_heads, page_size, head_dim):
