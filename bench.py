@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+PEAK_PCIE_GBS = 64.0       # host link, per direction
 
 WORKLOAD_TEXT = {
     "C2": "3-layer bf16 HSTU stack, full recompute (no cache): batch 8, d_model 512, 4 heads x 128, "
@@ -172,6 +173,9 @@ def main(argv=None):
                  "unmasked_pairs_per_head": int(req_last.info.pairs)})
     req_last.close()
 
+    n_evicted = int(len(scn_evicted(scn, users, new_len)))
+    tier = host_tier_rates(scn) if scn.cache is not None else None   # attaches a host tier: last
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, scn, users, new_len, n_targets, norm_n, rows)
@@ -194,16 +198,59 @@ def main(argv=None):
                    "new_tokens_per_step": n_new,
                    "candidate_tokens_per_step": int(sum(n_targets)),
                    "cached_key_fraction": round(cached_frac, 4),
-                   "evicted_users_per_step": int(len(scn_evicted(scn, users, new_len))),
+                   "evicted_users_per_step": n_evicted,
                    "attention_work_items": int(info0.n_work_items), "seed": args.seed},
         "roofline": roof,
         "kernels": kern,
         "kernel_ms_per_step": round(sum(k["ms_per_step"] for k in kern.values()), 4),
         "ms_per_step_event_instrumented": round(ms_instrumented, 4),
         "candidate_tokens_per_s": round(sum(n_targets) / (ms_per_step / 1000.0), 1),
+        "host_tier": tier,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def host_tier_rates(scn, reps=3):
+    """Host-tier copies outside the timed region: every cached user of the
+    pre-request state is offloaded to a pinned host tier that just holds them,
+    then onboarded back, `reps` times.  Rate = K and V bytes of every layer of
+    the moved pages / the event-timed duration of the call's GPU work (one
+    tier-copy launch).  The cache is left with a host tier attached."""
+    import torch
+
+    from generative_recommender_sequence_amd import hstu, runtime
+    cache, w = scn.cache, scn.w
+    scn.restore()
+    ids = [int(u) for u, h in zip(w.user_ids, w.hit) if h] + [int(u) for u in w.stale_ids]
+    where, lens = hstu.kv_residency(cache.h, ids)
+    ids = [u for u, wh in zip(ids, where) if wh == 1]
+    pages = sum(-(-int(n) // cache.page_size) for n, wh in zip(lens, where) if wh == 1)
+    if not pages:
+        return None
+    es = 2 if cache.dtype == hstu.HSTU_BF16 else 4
+    moved = pages * cache.num_layers * 2 * cache.num_heads * cache.page_size * cache.head_dim * es
+    cache.attach_host(pages)
+    s = runtime.stream_handle()
+    times = {"offload": [], "onboard": []}
+    for _ in range(reps):
+        for kind in ("offload", "onboard"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if kind == "offload":
+                hstu.kv_offload(cache.h, ids, s)
+            else:
+                hstu.kv_onboard(cache.h, ids, s)
+            e1.record()
+            e1.synchronize()
+            times[kind].append(e0.elapsed_time(e1))
+    out = {"users": len(ids), "pages": pages, "bytes_per_call": moved, "link": "PCIe 5.0 x16",
+           "link_peak_GBps_per_direction": PEAK_PCIE_GBS}
+    for kind, ts in times.items():
+        ms = sorted(ts)[len(ts) // 2]
+        out[f"{kind}_ms"] = round(ms, 3)
+        out[f"{kind}_GBps"] = round(moved / (ms * 1e-3) / 1e9, 2)
+    return out
 
 
 def scn_evicted(scn, users, new_len):
