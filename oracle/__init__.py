@@ -78,6 +78,9 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     lib.oracle_layer.restype = ctypes.c_int
     lib.oracle_layer.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_double] + [i64p] * 3 + [f64p] +
                                  [f64p] + [f32p] * 3 + [ctypes.c_int, i64p, f64p, f64p] + [f64p] * 8)
+    lib.oracle_head.restype = ctypes.c_int
+    lib.oracle_head.argtypes = [f64p, ctypes.c_int64, ctypes.c_int, i32p, ctypes.c_int64, ctypes.c_int,
+                                ctypes.c_int] + [f64p] * 5
     lib.oracle_kv_create.restype = vp
     lib.oracle_kv_create.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p]
     lib.oracle_kv_destroy.restype = None
@@ -210,6 +213,30 @@ def layer(x, w1, w2, rab, new_len, start, n_targets, norm_n, hist_k, hist_v, num
     if rc != OK:
         raise ValueError(f"oracle_layer rc={rc}")
     return out
+
+
+def head(y, rows, a, b, w, c, mutant: int = 0) -> np.ndarray:
+    """Multitask ranking head: logits [len(rows)][tasks] of rows `rows` of y
+    [*][d]; a [tasks][d][hidden], b [tasks][hidden], w [tasks][hidden], c
+    [tasks] (see oracle_head in hstu_oracle.c for the formula)."""
+    y, a, b, w, c = (_f64(t) for t in (y, a, b, w, c))
+    rows = np.ascontiguousarray(np.asarray(rows, np.int32))
+    tasks, d, hidden = a.shape
+    out = np.zeros((len(rows), tasks))
+    rc = load(mutant).oracle_head(_p(y, ctypes.c_double), y.shape[0], d, _p(rows, ctypes.c_int32), len(rows),
+                                  tasks, hidden, _p(a, ctypes.c_double), _p(b, ctypes.c_double),
+                                  _p(w, ctypes.c_double), _p(c, ctypes.c_double), _p(out, ctypes.c_double))
+    if rc != OK:
+        raise ValueError(f"oracle_head: status {rc}")
+    return out
+
+
+def candidate_rows(new_len, n_targets) -> np.ndarray:
+    """Rows of the new-token matrix holding each user's candidates (the last
+    min(T_u, t_u) new tokens of each user), in batch order."""
+    off = offsets(new_len)
+    return np.concatenate([np.arange(off[b + 1] - min(int(n_targets[b]), int(new_len[b])), off[b + 1])
+                           for b in range(len(new_len))] + [np.zeros(0, np.int64)]).astype(np.int32)
 
 
 class UserCache:

@@ -21,6 +21,9 @@
  *   M(i) = {j <= i} for history queries, {j < history length} u {i} for
  *   candidate queries; b(delta) = min(nb-1, floor(4 log2(1+delta))).
  *
+ *   Multitask ranking head (see oracle_head): per scored row and task, a
+ *   Linear -> ReLU -> Linear perceptron giving the task's logit.
+ *
  *   KV cache ("Deploying an HSTU Generative Recommender with NVIDIA
  *   Dynamo-Triton": a paged KV data table with lookup, allocation, append and
  *   eviction, LRU-style eviction of older users when space is tight; the
@@ -308,5 +311,62 @@ int oracle_layer(int B, int d, int H, int dh, double eps, const int64_t *q_off,
       for (int c = 0; c < d; ++c) xhat_out[r * d + c] = xh[r * d + c];
   }
   free(xh); free(s); free(o); free(g); free(kv_off); free(kf); free(vf); free(qn);
+  return OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* multitask ranking head ("NVIDIA Dynamo-Triton Gets End-to-End HSTU      */
+/* Generative Recommender Workflow", section Recommendation as sequence      */
+/* modeling: in the HSTU ranking example the blocks process the sequence    */
+/* and a prediction head yields multitask ranking outputs).  The pages name */
+/* no tasks or head shape; the reading here: for each scored row y (a row   */
+/* of the last block's output) and task t, a two-layer perceptron           */
+/*   z_t = c_t + sum_j w_t[j] * ReLU(b_t[j] + sum_k y[k] * A_t[k][j])        */
+/* with A_t [d][hidden], b_t, w_t [hidden] and c_t; z is the task's logit.   */
+/* ------------------------------------------------------------------------ */
+int oracle_head(const double *y, int64_t y_rows, int d, const int32_t *rows, int64_t n_rows, int tasks,
+                int hidden, const double *a, const double *b, const double *w, const double *c,
+                double *logits) {
+  if (!y || d <= 0 || tasks <= 0 || hidden <= 0 || n_rows < 0 || (n_rows > 0 && (!rows || !logits)))
+    return ERR_INVALID;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= y_rows) return ERR_INVALID;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+#if ORACLE_MUTANT == 16
+    const double *yr = y + r * d; /* planted: the row list ignored */
+#else
+    const double *yr = y + (int64_t)rows[r] * d;
+#endif
+    for (int t = 0; t < tasks; ++t) {
+      const double *at = a + (int64_t)t * d * hidden;
+#if ORACLE_MUTANT == 15
+      double z = c[0]; /* planted: task 0's output bias for every task */
+#else
+      double z = c[t];
+#endif
+      for (int j = 0; j < hidden; ++j) {
+#if ORACLE_MUTANT == 13
+        double pre = 0.0; /* planted: hidden bias dropped */
+#else
+        double pre = b[(int64_t)t * hidden + j];
+#endif
+        for (int k = 0; k < d; ++k) {
+#if ORACLE_MUTANT == 14
+          pre += yr[k] * at[(int64_t)j * d + k]; /* planted: A_t read transposed */
+#else
+          pre += yr[k] * at[(int64_t)k * hidden + j];
+#endif
+        }
+#if ORACLE_MUTANT == 12
+        double h = pre < 0.0 ? pre : 0.0; /* planted: ReLU's sign flipped */
+#else
+        double h = pre > 0.0 ? pre : 0.0;
+#endif
+        z += w[(int64_t)t * hidden + j] * h;
+      }
+      logits[r * tasks + t] = z;
+    }
+  }
   return OK;
 }

@@ -1,7 +1,7 @@
 """Pins of the CPU oracle against things other than itself.
 
 Each pin returns (ok, detail) for a given oracle build (mutant 0 = the real
-oracle; mutants 1..11 each plant one deliberate mistake, see hstu_oracle.c).
+oracle; mutants 1..16 each plant one deliberate mistake, see hstu_oracle.c).
 test_oracle.py asserts that the real oracle passes every pin and that every
 mutant fails at least one, so a plausible slip anywhere in the oracle (a wrong
 sign, a dropped term, an index off by one, a transposed operand, swapped
@@ -23,6 +23,10 @@ What pins what:
               move when future tokens change; a candidate's input moves only
               its own rows; cached prefix + append equals full recompute
               bit for bit; a jagged batch equals each user run alone
+  head        torch.nn Linear -> ReLU -> Linear per task (float64); the
+              affine closed form when every hidden unit is active and the
+              output bias alone when none is; the row list against scoring
+              rows one at a time
 """
 from __future__ import annotations
 
@@ -235,5 +239,58 @@ def pin_jagged(m=0):
     return ok, "jagged == alone"
 
 
+def _head_case(seed, n=7, d=6, tasks=3, hidden=5):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n, d)), rng.standard_normal((tasks, d, hidden)), rng.standard_normal((tasks, hidden)),
+            rng.standard_normal((tasks, hidden)), rng.standard_normal(tasks))
+
+
+def pin_head_torch(m=0):
+    """Each task's logit equals torch.nn's Linear -> ReLU -> Linear (float64)
+    built from the task's weights; d != hidden, so a transposed read fails."""
+    y, a, b, w, c = _head_case(1)
+    rows = [4, 0, 6, 2]
+    got = oracle.head(y, rows, a, b, w, c, m)
+    want = np.zeros_like(got)
+    for t in range(a.shape[0]):
+        mlp = torch.nn.Sequential(torch.nn.Linear(a.shape[1], a.shape[2]), torch.nn.ReLU(),
+                                  torch.nn.Linear(a.shape[2], 1)).double()
+        with torch.no_grad():
+            mlp[0].weight.copy_(torch.from_numpy(a[t].T.copy()))
+            mlp[0].bias.copy_(torch.from_numpy(b[t]))
+            mlp[2].weight.copy_(torch.from_numpy(w[t][None, :]))
+            mlp[2].bias.copy_(torch.tensor([c[t]], dtype=torch.float64))
+            want[:, t] = mlp(torch.from_numpy(y[rows])).numpy()[:, 0]
+    err = _relerr(got, want)
+    return err < 1e-12, f"head vs torch.nn MLP rel err {err:.2e}"
+
+
+def pin_head_regimes(m=0):
+    """All hidden units active: the head is affine, z = y . (A_t w_t) + (b_t . w_t
+    + c_t), summed in the other order.  All inactive: z = c_t exactly."""
+    y, a, b, w, c = _head_case(2)
+    y = np.abs(y)
+    a = np.abs(a)
+    b = np.abs(b) + 1.0
+    rows = np.arange(y.shape[0])
+    got = oracle.head(y, rows, a, b, w, c, m)
+    want = np.stack([y @ (a[t] @ w[t]) + (b[t] @ w[t] + c[t]) for t in range(a.shape[0])], axis=1)
+    err = _relerr(got, want)
+    off = oracle.head(y, rows, a, -b - 100.0, w, c, m)
+    exact = bool(np.array_equal(off, np.broadcast_to(c, off.shape)))
+    return err < 1e-12 and exact, f"active rel err {err:.2e}, inactive exact {exact}"
+
+
+def pin_head_rows(m=0):
+    """Scoring a list of rows (with repeats) equals scoring every row alone
+    and picking them."""
+    y, a, b, w, c = _head_case(3)
+    rows = [5, 5, 1, 3]
+    got = oracle.head(y, rows, a, b, w, c, m)
+    singles = np.concatenate([oracle.head(y[r:r + 1], [0], a, b, w, c, m) for r in rows])
+    return bool(np.array_equal(got, singles)), "row gather"
+
+
 PINS = [pin_silu, pin_layer_norm, pin_bucket, pin_attention_closed_form, pin_layer_vs_brute,
-        pin_c1_vs_brute, pin_identity, pin_causal, pin_target_isolation, pin_cache, pin_jagged]
+        pin_c1_vs_brute, pin_identity, pin_causal, pin_target_isolation, pin_cache, pin_jagged,
+        pin_head_torch, pin_head_regimes, pin_head_rows]
