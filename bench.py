@@ -7,7 +7,7 @@ metadata to its pre-request state, look the batch up, evict least-recently
 used users if pages are short, allocate pages, upload the page table and the
 request plan, then run every layer (pre-norm, f1 + SiLU, K/V append,
 attention over cached + new keys, LayerNorm(AV) * U, f2 + residual) on the
-new tokens.  The new-token inputs are already in device memory when timing
+new tokens, and score the candidate rows with the multitask ranking head.  The new-token inputs are already in device memory when timing
 starts.  Prints one JSON line: new tokens per second, the dominant kernel
 against its roofline (duration from HIP events on its launch stream), and the
 CPU oracle timed on a bounded sample of the same workload.
@@ -84,7 +84,7 @@ def main(argv=None):
     import torch
 
     from generative_recommender_sequence_amd import hstu, profiling, runtime
-    from generative_recommender_sequence_amd.workloads import workload_for
+    from generative_recommender_sequence_amd.workloads import head_weights, workload_for
 
     runtime.require_gpu()
     torch.cuda.set_device(0)
@@ -105,12 +105,17 @@ def main(argv=None):
 
     rbufs = runtime.RequestBuffers(cfg.batch, scn.max_pages, int(info0.meta_bytes) + 4096)
     ybufs = [torch.empty_like(x), torch.empty_like(x)]
+    # the multitask ranking head scores every candidate row of the last layer
+    head = runtime.Head(head_weights(cfg.d_model, seed=args.seed), scn.dtype)
+    cand = torch.from_numpy(runtime.candidate_row_list(new_len, n_targets)).cuda()
+    logits = torch.empty((max(cand.numel(), 1), head.tasks), dtype=torch.float32, device="cuda")
 
     def step():
         scn.restore()
         req = runtime.prepare(scn.cache, users, new_len, n_targets, norm_n, scn.max_pages, cfg.num_heads,
                               cfg.head_dim, bufs=rbufs)
         y = runtime.forward(scn.model, req, x, scn.cache, ws, out_bufs=ybufs)
+        head(y, cand, out=logits)
         return req, y
 
     pending = []
@@ -199,7 +204,9 @@ def main(argv=None):
                    "candidate_tokens_per_step": int(sum(n_targets)),
                    "cached_key_fraction": round(cached_frac, 4),
                    "evicted_users_per_step": n_evicted,
-                   "attention_work_items": int(info0.n_work_items), "seed": args.seed},
+                   "attention_work_items": int(info0.n_work_items),
+                   "head": f"{head.tasks} tasks x MLP({cfg.d_model}-{head.hidden}-1) on every candidate row",
+                   "seed": args.seed},
         "roofline": roof,
         "kernels": kern,
         "kernel_ms_per_step": round(sum(k["ms_per_step"] for k in kern.values()), 4),

@@ -683,4 +683,54 @@ hstu_status hstu_stack_forward(const hstu_layer_args* layers, int32_t n, hipStre
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// multitask ranking head
+// ---------------------------------------------------------------------------
+
+namespace {
+hstu_status head_check(const hstu_head_args* a, size_t* need) {
+  if (!a) return fail(HSTU_ERR_INVALID, "hstu_head: null arguments");
+  if (a->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_head: only bf16 is supported");
+  if (a->d_model <= 0 || a->d_model % 64 != 0 || a->num_tasks <= 0 || a->hidden <= 0 ||
+      a->hidden % kHeadTile != 0 || a->n_rows < 0)
+    return fail(HSTU_ERR_INVALID, "hstu_head: d_model must be a multiple of 64, hidden of 128");
+  if (static_cast<int64_t>(a->num_tasks) * a->hidden > (1 << 30))
+    return fail(HSTU_ERR_INVALID, "hstu_head: too many hidden units");
+  *need = align256(static_cast<size_t>(a->n_rows) * a->num_tasks * (a->hidden / kHeadTile) * sizeof(float));
+  return ok();
+}
+}  // namespace
+
+hstu_status hstu_head_workspace_size(const hstu_head_args* a, size_t* bytes) {
+  if (!bytes) return fail(HSTU_ERR_INVALID, "hstu_head_workspace_size: null output");
+  return head_check(a, bytes);
+}
+
+hstu_status hstu_head_forward(const hstu_head_args* a, hipStream_t stream) {
+  size_t need = 0;
+  hstu_status st = head_check(a, &need);
+  if (st != HSTU_OK) return st;
+  if (a->n_rows == 0) return ok();
+  if (a->y_rows <= 0 || !a->y || !a->d_rows || !a->w_hidden || !a->b_hidden || !a->w_out || !a->b_out ||
+      !a->logits)
+    return fail(HSTU_ERR_INVALID, "hstu_head_forward: null buffer or no rows in y");
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(HSTU_ERR_INVALID, "hstu_head_forward: workspace too small");
+  HeadArgs h{};
+  h.y = a->y;
+  h.y_rows = a->y_rows;
+  h.d = a->d_model;
+  h.rows = a->d_rows;
+  h.n_rows = a->n_rows;
+  h.tasks = a->num_tasks;
+  h.hidden = a->hidden;
+  h.w_hidden = a->w_hidden;
+  h.b_hidden = a->b_hidden;
+  h.w_out = a->w_out;
+  h.b_out = a->b_out;
+  h.logits = a->logits;
+  h.partial = static_cast<float*>(a->workspace);
+  return check_hip(timed(TK_HEAD, stream, [&] { return launch_head_bf16(h, stream); }), "hstu_head_forward");
+}
+
 }  // extern "C"

@@ -116,7 +116,7 @@ struct hstu_kv_cache {
 namespace hstu {
 
 // ---- optional event timing of launches (hstu_timing_*) ---------------------
-enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_COUNT };
+enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_HEAD, TK_COUNT };
 // Brackets one launch: records a start event now and an end event when the
 // returned guard's end() is called (both on stream s), if timing is enabled.
 struct TimedLaunch {
@@ -228,5 +228,23 @@ struct F1Args {
 // [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row stats, routed per F1Args
 hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
                           const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s);
+
+// Multitask ranking head on rows of y (bf16 [y_rows][d]): per task t and
+// listed row, logit = b_out[t] + sum_j w_out[t][j] * ReLU(b_hidden[t][j] +
+// y_row . w_hidden[t hidden + j]); w_hidden output-major [tasks*hidden][d].
+constexpr int kHeadTile = 128;  // hidden columns per block (hidden % kHeadTile == 0)
+struct HeadArgs {
+  const void* y;
+  int32_t y_rows, d;
+  const int32_t* rows;  // [n_rows] (clamped to [0, y_rows))
+  int32_t n_rows, tasks, hidden;
+  const void* w_hidden;
+  const float* b_hidden;  // [tasks*hidden]
+  const float* w_out;     // [tasks*hidden]
+  const float* b_out;     // [tasks]
+  float* logits;          // [n_rows][tasks]
+  float* partial;         // [n_rows][tasks*hidden/kHeadTile] scratch
+};
+hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s);
 
 }  // namespace hstu

@@ -23,6 +23,11 @@
 // same buffer (contiguous keys) or straight into their pages (paged cache; the
 // append of the new tokens).
 //
+// Epilogue 2 is the multitask ranking head's hidden layer and output dot
+// product: A's rows are gathered through a row list, each column n gets
+// ReLU(acc + b[n]) * w[n], and the block sums its BN columns per row into one
+// partial logit; a small kernel adds a task's partials and its output bias.
+//
 // fp32: plain 64 x 64-tile FMA kernels, with the pre-norm done by a separate
 // row LayerNorm and the append by the copy kernel.
 #include "common.h"
@@ -56,6 +61,12 @@ struct F1Route {
   uint16_t* v_pool;
   int64_t pool_layer_offset;  // elements
   int32_t dh, page_size;
+  // epilogue 2 (head)
+  const int32_t* a_rows;      // [M]: the row of A that output row m reads
+  int32_t a_rows_max;         // rows of A; indices are clamped to [0, a_rows_max)
+  const float* h_bias;        // [N] hidden bias
+  const float* h_wout;        // [N] output weights
+  float* h_partial;           // [M][N / BN] partial logits
 };
 
 template <int BM, int BN, int EPI>
@@ -93,12 +104,21 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   // copy: instruction j of the block fills rows 8 j .. 8 j + 7 (1 KB); lane l
   // carries row 8 j + l / 8, chunk slot l % 8, i.e. logical chunk slot ^ swz8(row)
   const int crow = lane >> 3, cslot = lane & 7;
+  int64_t a_src[BM / 32];  // epilogue 2: gathered source rows, looked up once
+  if (EPI == 2) {
+#pragma unroll
+    for (int i = 0; i < BM / 32; ++i) {
+      const int src = route.a_rows[min(m0 + 8 * (wave + 4 * i) + crow, M - 1)];
+      a_src[i] = static_cast<int64_t>(min(max(src, 0), route.a_rows_max - 1)) * K;
+    }
+  }
   auto copy_k = [&](int k0, lds_u16* Ad, lds_u16* Bd) {
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) {
       const int r = 8 * (wave + 4 * i) + crow;
       const int m = min(m0 + r, M - 1);  // rows past M repeat the last row
-      dma16(A + static_cast<int64_t>(m) * K + k0 + 8 * (cslot ^ swz8(r)), Ad + 8 * (wave + 4 * i) * GBK);
+      const int64_t row_off = EPI == 2 ? a_src[i] : static_cast<int64_t>(m) * K;
+      dma16(A + row_off + k0 + 8 * (cslot ^ swz8(r)), Ad + 8 * (wave + 4 * i) * GBK);
     }
 #pragma unroll
     for (int i = 0; i < BN / 32; ++i) {
@@ -142,9 +162,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   // k loop: each lane's row records (f1) or residual values (f2), and the
   // block's column sums (f1, into LDS)
   __shared__ __attribute__((aligned(16))) float cs_lds[EPI == 0 ? BN : 4];
+  __shared__ __attribute__((aligned(16))) float hb_lds[EPI == 2 ? BN : 4];
+  __shared__ __attribute__((aligned(16))) float hw_lds[EPI == 2 ? BN : 4];
   RowInfo rinfo[MT];
   u32x2 resid[MT][NT][4];
-  if (EPI == 0) {
+  if (EPI == 2) {
+    if (tid < BN / 4) {
+      *reinterpret_cast<f32x4*>(&hb_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.h_bias[n0 + 4 * tid]);
+      *reinterpret_cast<f32x4*>(&hw_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.h_wout[n0 + 4 * tid]);
+    }
+  } else if (EPI == 0) {
     if (tid < BN / 4)
       *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.colsum[n0 + 4 * tid]);
 #pragma unroll
@@ -175,6 +202,32 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     __builtin_amdgcn_sched_barrier(0);
     mma_k(A1, B1);
     __syncthreads();  // buffer 0 filled; buffer 1 free
+  }
+
+  if (EPI == 2) {
+    // each lane sums ReLU(acc + b) * w over its 16 NT columns of row l32; the
+    // two lane halves and then the two column waves are added in fixed order
+    __shared__ float red[2][BM];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * (BN / 2) + 32 * j + 8 * q + 4 * g;
+          const f32x4 hb = *reinterpret_cast<const f32x4*>(&hb_lds[nl]);
+          const f32x4 hw = *reinterpret_cast<const f32x4*>(&hw_lds[nl]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum += fmaxf(acc[i][j][4 * q + e] + hb[e], 0.f) * hw[e];
+        }
+      sum += __shfl_xor(sum, 32);
+      if (g == 0) red[wn][wm * (BM / 2) + 32 * i + l32] = sum;
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < M)
+      route.h_partial[static_cast<int64_t>(m0 + tid) * (N / BN) + n0 / BN] = red[0][tid] + red[1][tid];
+    return;
   }
 
   // epilogue: lane owns row m = ... + l32 and columns n = ... + 8 (r/4) + 4 g + [0, 4)
@@ -356,6 +409,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     }
 }
 
+// logits[m][t] = c[t] + the task's partials (in column order)
+__global__ __launch_bounds__(256) void head_finalize_kernel(const float* __restrict__ partial,
+                                                           int32_t per_task, int32_t tasks,
+                                                           const float* __restrict__ c,
+                                                           float* __restrict__ logits, int32_t M) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * tasks) return;
+  const int t = static_cast<int>(idx % tasks);
+  const float* p = partial + idx * per_task;
+  float z = c[t];
+  for (int k = 0; k < per_task; ++k) z += p[k];
+  logits[idx] = z;
+}
+
 }  // namespace
 
 hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
@@ -395,6 +462,33 @@ hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsu
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1t),
                      static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s) {
+  if (h.n_rows == 0) return hipSuccess;
+  constexpr int BN = kHeadTile;
+  const int32_t N = h.tasks * h.hidden;
+  if (h.hidden % BN != 0 || h.d % GBK != 0 || h.y_rows <= 0) return hipErrorInvalidValue;
+  F1Route r{};
+  r.a_rows = h.rows;
+  r.a_rows_max = h.y_rows;
+  r.h_bias = h.b_hidden;
+  r.h_wout = h.w_out;
+  r.h_partial = h.partial;
+  const auto* y = static_cast<const uint16_t*>(h.y);
+  const auto* wt = static_cast<const uint16_t*>(h.w_hidden);
+  if (h.n_rows >= 8192)
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, BN, 2>), dim3(gemm_grid<128, BN>(h.n_rows, N)), dim3(256), 0, s, y,
+                       wt, nullptr, nullptr, r, h.n_rows, N, h.d);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 2>), dim3(gemm_grid<64, BN>(h.n_rows, N)), dim3(256), 0, s, y,
+                       wt, nullptr, nullptr, r, h.n_rows, N, h.d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t outs = static_cast<int64_t>(h.n_rows) * h.tasks;
+  hipLaunchKernelGGL(head_finalize_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)), dim3(256), 0, s,
+                     h.partial, h.hidden / BN, h.tasks, h.b_out, h.logits, h.n_rows);
   return hipGetLastError();
 }
 

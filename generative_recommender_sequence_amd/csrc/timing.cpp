@@ -11,7 +11,7 @@ namespace hstu {
 namespace {
 
 const char* kNames[TK_COUNT] = {"layer_norm", "f1_gemm",  "append", "attention",
-                                "reduce_gate", "f2_gemm", "gather"};
+                                "reduce_gate", "f2_gemm", "gather", "head"};
 
 struct TimingState {
   std::mutex mu;

@@ -61,6 +61,13 @@ class hstu_layer_args(ctypes.Structure):
                 ("workspace_bytes", c_size), ("uvqk_out", c_vp), ("o_out", c_vp), ("g_out", c_vp)]
 
 
+class hstu_head_args(ctypes.Structure):
+    _fields_ = [("dtype", c_i32), ("d_model", c_i32), ("num_tasks", c_i32), ("hidden", c_i32), ("y", c_vp),
+                ("y_rows", c_i32), ("d_rows", c_vp), ("n_rows", c_i32), ("w_hidden", c_vp), ("b_hidden", c_vp),
+                ("w_out", c_vp), ("b_out", c_vp), ("logits", c_vp), ("workspace", c_vp),
+                ("workspace_bytes", c_size)]
+
+
 # name -> (restype, argtypes); every symbol include/hstu.h declares
 SIGNATURES = {
     "hstu_last_error": (ctypes.c_char_p, []),
@@ -90,11 +97,13 @@ SIGNATURES = {
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
     "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
+    "hstu_head_workspace_size": (c_i32, [ctypes.POINTER(hstu_head_args), ctypes.POINTER(c_size)]),
+    "hstu_head_forward": (c_i32, [ctypes.POINTER(hstu_head_args), c_vp]),
     "hstu_timing_enable": (c_i32, [c_i32]),
     "hstu_timing_read": (c_i32, [ctypes.c_char_p, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
 
-TIMED_KERNELS = ("layer_norm", "f1_gemm", "append", "attention", "reduce_gate", "f2_gemm", "gather")
+TIMED_KERNELS = ("layer_norm", "f1_gemm", "append", "attention", "reduce_gate", "f2_gemm", "gather", "head")
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -393,6 +402,16 @@ def hstu_stack_forward(layers, stream: int):
     else:
         arr = layers
     _check(lib().hstu_stack_forward(arr, len(arr), stream), "hstu_stack_forward")
+
+
+def hstu_head_workspace_size(args: hstu_head_args) -> int:
+    n = c_size(0)
+    _check(lib().hstu_head_workspace_size(ctypes.byref(args), ctypes.byref(n)), "hstu_head_workspace_size")
+    return n.value
+
+
+def hstu_head_forward(args: hstu_head_args, stream: int):
+    _check(lib().hstu_head_forward(ctypes.byref(args), stream or None), "hstu_head_forward")
 
 
 def hstu_timing_enable(enable: bool):

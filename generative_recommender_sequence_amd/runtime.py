@@ -272,6 +272,53 @@ def forward(model: Model, req: Request, x: torch.Tensor, cache: Optional[PagedCa
     return cur
 
 
+class Head:
+    """Device copies of a multitask ranking head in the library's layout:
+    w_hidden output-major [tasks*hidden][d] (row t*hidden + j = task t's
+    column j), b_hidden and w_out flat fp32 [tasks*hidden], b_out [tasks]."""
+
+    def __init__(self, hw, dtype: int, device="cuda"):
+        tasks, d, hidden = hw.a.shape
+        self.dtype, self.tasks, self.hidden, self.d_model = dtype, tasks, hidden, d
+        wt = np.ascontiguousarray(np.transpose(hw.a, (0, 2, 1)).reshape(tasks * hidden, d))
+        self.w_hidden = torch.from_numpy(wt).to(device=device, dtype=tdtype(dtype))
+        self.b_hidden = torch.from_numpy(np.ascontiguousarray(hw.b, np.float32).reshape(-1)).to(device)
+        self.w_out = torch.from_numpy(np.ascontiguousarray(hw.w, np.float32).reshape(-1)).to(device)
+        self.b_out = torch.from_numpy(np.ascontiguousarray(hw.c, np.float32)).to(device)
+        self.workspace = torch.empty(256, dtype=torch.uint8, device=device)
+
+    def args(self, y: torch.Tensor, rows: torch.Tensor, n_rows: int, logits: torch.Tensor) -> hstu.hstu_head_args:
+        a = hstu.hstu_head_args()
+        a.dtype, a.d_model, a.num_tasks, a.hidden = self.dtype, self.d_model, self.tasks, self.hidden
+        a.y, a.y_rows = y.data_ptr(), y.shape[0]
+        a.d_rows, a.n_rows = rows.data_ptr(), n_rows
+        a.w_hidden, a.b_hidden = self.w_hidden.data_ptr(), self.b_hidden.data_ptr()
+        a.w_out, a.b_out, a.logits = self.w_out.data_ptr(), self.b_out.data_ptr(), logits.data_ptr()
+        need = hstu.hstu_head_workspace_size(a)
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(2 * need, dtype=torch.uint8, device=y.device)
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        return a
+
+    def __call__(self, y: torch.Tensor, rows: torch.Tensor, n_rows: Optional[int] = None, stream=None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Logits [n_rows, tasks] fp32 of rows `rows` (device int32) of y."""
+        n = rows.numel() if n_rows is None else n_rows
+        logits = out if out is not None else torch.empty((max(n, 1), self.tasks), dtype=torch.float32,
+                                                         device=y.device)
+        hstu.hstu_head_forward(self.args(y, rows, n, logits), stream_handle(stream))
+        return logits[:n]
+
+
+def candidate_row_list(new_len, n_targets) -> np.ndarray:
+    """The new-token rows of each user's candidates: its last min(T_u, t_u)
+    new tokens, users in batch order."""
+    ends = np.cumsum(np.asarray(new_len, np.int64))
+    take = np.minimum(np.asarray(n_targets, np.int64), np.asarray(new_len, np.int64))
+    parts = [np.arange(e - t, e) for e, t in zip(ends, take)]
+    return np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+
+
 def attention(req: Request, q: torch.Tensor, q_row_stride: int, rab: torch.Tensor, dtype: int,
               k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, kv_row_stride: int = 0,
               cache: Optional[PagedCache] = None, layer: int = 0, stream=None) -> torch.Tensor:

@@ -99,6 +99,34 @@ class LayerWeights:
 
 
 @dataclass
+class HeadWeights:
+    """Multitask ranking head, per task t: a [t] [d][hidden] first-layer
+    weights (bf16-exact in bf16 workloads), b [t] [hidden] hidden bias, w [t]
+    [hidden] output weights, c [t] output bias."""
+    a: np.ndarray
+    b: np.ndarray
+    w: np.ndarray
+    c: np.ndarray
+
+
+HEAD_TASKS, HEAD_HIDDEN = 4, 256
+
+
+def head_weights(d_model: int, tasks: int = HEAD_TASKS, hidden: int = HEAD_HIDDEN, seed: int = 0,
+                 dtype: str = "bf16") -> HeadWeights:
+    """Seeded synthetic head weights: N(0, 1/d) first layer (unit-scale hidden
+    pre-activations for unit-scale rows), N(0, 0.01) biases, N(0, 1/hidden)
+    output weights."""
+    rng = np.random.default_rng([seed, 0x4EAD])
+    rnd = round_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    a = rnd(rng.standard_normal((tasks, d_model, hidden)) / np.sqrt(d_model))
+    b = (rng.standard_normal((tasks, hidden)) * 0.1).astype(np.float32)
+    w = (rng.standard_normal((tasks, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    c = (rng.standard_normal(tasks) * 0.1).astype(np.float32)
+    return HeadWeights(a, b, w, c)
+
+
+@dataclass
 class Workload:
     cfg: Config
     seed: int

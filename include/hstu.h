@@ -323,13 +323,52 @@ hstu_status hstu_layer_forward(const hstu_layer_args *args, hipStream_t stream);
 hstu_status hstu_stack_forward(const hstu_layer_args *layers, int32_t n, hipStream_t stream);
 
 /* ======================================================================== */
+/* Multitask ranking head ["NVIDIA Dynamo-Triton Gets End-to-End HSTU       */
+/* Generative Recommender Workflow", section Recommendation as sequence     */
+/* modeling: a prediction head on the HSTU blocks' output gives multitask   */
+/* ranking outputs]                                                          */
+/* ======================================================================== */
+
+/* The pages name neither the tasks nor the head's shape.  Here, for each
+ * listed row y (a row of the last layer's output, normally a candidate's)
+ * and each task t, a two-layer perceptron gives the task's logit:
+ *     logit[r][t] = b_out[t] + sum_j w_out[t][j] * ReLU(b_hidden[t][j] + y . A_t[:, j])
+ * (A_t: task t's [d_model][hidden] first-layer weights).  bf16 MFMA with fp32
+ * accumulation; bias, output weights and logits fp32. */
+typedef struct {
+  hstu_dtype dtype;          /* HSTU_BF16 (HSTU_F32: UNSUPPORTED) */
+  int32_t d_model;           /* multiple of 64 */
+  int32_t num_tasks;         /* >= 1 */
+  int32_t hidden;            /* per task, a multiple of 128 */
+  const void *y;             /* device [y_rows][d_model] dtype, rows contiguous, 16-byte aligned */
+  int32_t y_rows;
+  const int32_t *d_rows;     /* device int32 [n_rows]: rows of y to score (clamped to [0, y_rows)) */
+  int32_t n_rows;
+  /* weights, output-major: row t*hidden + j of w_hidden [num_tasks*hidden][d_model]
+   * (dtype) is A_t[:, j]; b_hidden, w_out fp32 [num_tasks*hidden] (task-major);
+   * b_out fp32 [num_tasks].  Device, 16-byte aligned. */
+  const void *w_hidden;
+  const float *b_hidden;
+  const float *w_out;
+  const float *b_out;
+  float *logits;             /* device out fp32 [n_rows][num_tasks] */
+  void *workspace;           /* device, >= hstu_head_workspace_size */
+  size_t workspace_bytes;
+} hstu_head_args;
+
+hstu_status hstu_head_workspace_size(const hstu_head_args *args, size_t *bytes);
+/* Enqueues the head on `stream` (n_rows == 0: nothing).  INVALID for bad
+ * sizes or NULL buffers, UNSUPPORTED for fp32. */
+hstu_status hstu_head_forward(const hstu_head_args *args, hipStream_t stream);
+
+/* ======================================================================== */
 /* Instrumentation: kernel durations measured with HIP events               */
 /* ======================================================================== */
 
 /* When enabled (non-zero), every kernel the library launches is bracketed
  * by a pair of HIP events recorded on the stream it is launched on.  Kernel
  * names: "layer_norm", "f1_gemm", "append", "attention", "reduce_gate",
- * "f2_gemm", "gather".  Enabling or disabling clears the records. */
+ * "f2_gemm", "gather", "head".  Enabling or disabling clears the records. */
 hstu_status hstu_timing_enable(int32_t enable);
 /* Waits for the recorded events of `kernel` and returns the number of
  * launches and their summed duration in milliseconds; clears them.

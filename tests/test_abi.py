@@ -91,3 +91,29 @@ def test_plan_rejects_use_before_upload():
     assert _status(hstu.hstu_attn_fwd, args, 0) == HSTU_ERR_INVALID
     assert b"not uploaded" in hstu.lib().hstu_last_error()
     hstu.hstu_plan_destroy(p)
+
+
+def test_head_validation_and_workspace():
+    a = hstu.hstu_head_args()
+    a.dtype, a.d_model, a.num_tasks, a.hidden, a.n_rows = HSTU_BF16, 512, 4, 256, 1000
+    # one partial logit per (row, task, 128 hidden units), 256-aligned
+    assert hstu.hstu_head_workspace_size(a) == 1000 * 4 * 2 * 4
+    a.n_rows = 0
+    hstu.hstu_head_forward(a, 0)                                   # nothing to do, no device call
+    a.n_rows = 3
+    assert _status(hstu.hstu_head_forward, a, 0) == HSTU_ERR_INVALID     # NULL buffers
+    a.hidden = 200
+    assert _status(hstu.hstu_head_workspace_size, a) == HSTU_ERR_INVALID
+    a.hidden, a.d_model = 256, 100
+    assert _status(hstu.hstu_head_workspace_size, a) == HSTU_ERR_INVALID
+    a.d_model, a.dtype = 512, 0
+    assert _status(hstu.hstu_head_forward, a, 0) == HSTU_ERR_UNSUPPORTED
+
+
+def test_candidate_row_list():
+    from generative_recommender_sequence_amd import runtime
+    import oracle
+    new_len, n_targets = [5, 3, 0, 64, 2], [2, 3, 4, 64, 5]
+    got = runtime.candidate_row_list(new_len, n_targets)
+    assert got.tolist() == [3, 4, 5, 6, 7] + list(range(8, 72)) + [72, 73]
+    assert np.array_equal(got, oracle.candidate_rows(new_len, n_targets))
