@@ -64,6 +64,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="C4", choices=["C2", "C3", "C4", "C5"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serving", action="store_true", help="skip the serving-loop latency measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (reference for HBM traffic counters)")
     args = ap.parse_args(argv)
@@ -179,6 +180,9 @@ def main(argv=None):
     req_last.close()
 
     n_evicted = int(len(scn_evicted(scn, users, new_len)))
+    serving_out = None
+    if not args.no_serving and args.workload == "C4":
+        serving_out = serving_results(w, args.seed)
     tier = host_tier_rates(scn) if scn.cache is not None else None   # attaches a host tier: last
 
     cpu = None
@@ -213,6 +217,7 @@ def main(argv=None):
         "ms_per_step_event_instrumented": round(ms_instrumented, 4),
         "candidate_tokens_per_s": round(sum(n_targets) / (ms_per_step / 1000.0), 1),
         "host_tier": tier,
+        "serving": serving_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -257,6 +262,41 @@ def host_tier_rates(scn, reps=3):
         ms = sorted(ts)[len(ts) // 2]
         out[f"{kind}_ms"] = round(ms, 3)
         out[f"{kind}_GBps"] = round(moved / (ms * 1e-3) / 1e9, 2)
+    return out
+
+
+def serving_results(w, seed, users=32):
+    """Latency under load of the serving loop (dynamic batches of up to 8,
+    500 us batching delay, host cache work overlapped with the previous
+    batch): a population of `users` users with the workload's history
+    distribution, each request bringing 0-16 new history events and 64
+    candidates; the device pool holds about half the population, so misses
+    (evicted users) recompute their history.  Capacity = throughput with every
+    request queued at once; then Poisson arrivals at 50% and 80% of it.  With
+    a host tier attached, evicted users are offloaded and onboarded instead."""
+    from generative_recommender_sequence_amd import serving
+
+    cfg = w.cfg
+    out = {"users": users, "max_batch": 8, "max_delay_us": 500, "in_flight": 2}
+    for label, host in (("device_cache", False), ("with_host_tier", True)):
+        rng = np.random.default_rng([seed, 77])
+        pop = serving.Population.draw(rng, users, cfg, events=(0, 16))
+        longest = pop.max_hist + 16 + cfg.n_targets
+        max_pages = -(-longest // cfg.page_size)
+        half = sum(-(-(int(h) + 16 + cfg.n_targets) // cfg.page_size) for h in pop.hist) // 2
+        pages = max(half, 8 * max_pages)
+        host_pages = 2 * users * max_pages if host else 0
+        srv = serving.Server(cfg, w.layers, pop, pages, host_pages=host_pages, seed=seed)
+        srv.run(serving.poisson_arrivals(rng, pop, float("inf"), 160))            # warm the cache
+        cap = srv.run(serving.poisson_arrivals(rng, pop, float("inf"), 800)).summary()
+        res = {"pool_pages": pages, "host_pages": host_pages, "capacity": cap}
+        for frac in (0.5, 0.8):
+            rate = frac * cap["throughput_req_per_s"]
+            res[f"load_{int(frac * 100)}pct"] = dict(
+                offered_req_per_s=round(rate, 1),
+                **srv.run(serving.poisson_arrivals(rng, pop, rate, 1200)).summary())
+        out[label] = res
+        del srv
     return out
 
 

@@ -68,6 +68,10 @@ class hstu_head_args(ctypes.Structure):
                 ("workspace_bytes", c_size)]
 
 
+class hstu_batcher_desc(ctypes.Structure):
+    _fields_ = [("max_batch", c_i32), ("max_delay_us", c_i64), ("max_tokens", c_i64)]
+
+
 # name -> (restype, argtypes); every symbol include/hstu.h declares
 SIGNATURES = {
     "hstu_last_error": (ctypes.c_char_p, []),
@@ -99,6 +103,11 @@ SIGNATURES = {
     "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
     "hstu_head_workspace_size": (c_i32, [ctypes.POINTER(hstu_head_args), ctypes.POINTER(c_size)]),
     "hstu_head_forward": (c_i32, [ctypes.POINTER(hstu_head_args), c_vp]),
+    "hstu_batcher_create": (c_i32, [ctypes.POINTER(hstu_batcher_desc), ctypes.POINTER(c_vp)]),
+    "hstu_batcher_destroy": (c_i32, [c_vp]),
+    "hstu_batcher_submit": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i64]),
+    "hstu_batcher_next": (c_i32, [c_vp, c_i64, P_i64, c_i32, P_i32, P_i64]),
+    "hstu_batcher_pending": (c_i32, [c_vp, P_i32]),
     "hstu_timing_enable": (c_i32, [c_i32]),
     "hstu_timing_read": (c_i32, [ctypes.c_char_p, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
@@ -414,6 +423,38 @@ def hstu_head_forward(args: hstu_head_args, stream: int):
     _check(lib().hstu_head_forward(ctypes.byref(args), stream or None), "hstu_head_forward")
 
 
+class Batcher:
+    """Owning wrapper of an hstu_batcher (host only)."""
+
+    def __init__(self, max_batch: int = 8, max_delay_us: int = 0, max_tokens: int = 0):
+        d = hstu_batcher_desc(max_batch, max_delay_us, max_tokens)
+        h = c_vp()
+        _check(lib().hstu_batcher_create(ctypes.byref(d), ctypes.byref(h)), "hstu_batcher_create")
+        self.h, self.max_batch = h.value, max_batch
+        self._ids = np.zeros(max_batch, np.int64)
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib().hstu_batcher_destroy(self.h)
+            self.h = None
+
+    def submit(self, request_id: int, user: int, n_new: int, arrival_us: int):
+        _check(lib().hstu_batcher_submit(self.h, int(request_id), int(user), int(n_new), int(arrival_us)),
+               "hstu_batcher_submit")
+
+    def next(self, now_us: int):
+        """(released request ids, wait_us)."""
+        n, wait = c_i32(0), c_i64(0)
+        _check(lib().hstu_batcher_next(self.h, int(now_us), _ptr(self._ids, c_i64), len(self._ids),
+                                       ctypes.byref(n), ctypes.byref(wait)), "hstu_batcher_next")
+        return [int(i) for i in self._ids[:n.value]], wait.value
+
+    def pending(self) -> int:
+        n = c_i32(0)
+        _check(lib().hstu_batcher_pending(self.h, ctypes.byref(n)), "hstu_batcher_pending")
+        return n.value
+
+
 def hstu_timing_enable(enable: bool):
     _check(lib().hstu_timing_enable(1 if enable else 0), "hstu_timing_enable")
 
@@ -431,7 +472,7 @@ def header_symbols(header_path: Optional[str] = None) -> Sequence[str]:
     import re
     if header_path is None:
         header_path = os.path.join(os.path.dirname(PKG), "include", "hstu.h")
-    text = open(header_path).read()
+    text = open(header_path, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                                  text, flags=re.M)))

@@ -362,6 +362,43 @@ hstu_status hstu_head_workspace_size(const hstu_head_args *args, size_t *bytes);
 hstu_status hstu_head_forward(const hstu_head_args *args, hipStream_t stream);
 
 /* ======================================================================== */
+/* Dynamic request batcher ["NVIDIA Dynamo-Triton Gets End-to-End HSTU      */
+/* Generative Recommender Workflow", section Five stages and the benchmark: */
+/* serving at dynamic batch size 8; "HSTU生成式推荐系统部署实战：NVIDIA      */
+/* Dynamo-Triton详解", Triton section: dynamic batching]                     */
+/* ======================================================================== */
+
+/* Host-only request queue.  A request is (request_id, user, n_new tokens,
+ * arrival time in microseconds on the caller's clock).  The next batch is
+ * read off the queue in submission order, skipping a request whose user is
+ * already in the batch (the KV cache takes each user once per request) and
+ * stopping at max_batch requests or before the first request that would take
+ * the batch past max_tokens new tokens (0: no limit; a first request is always
+ * taken).  The batch is released when no further request can join it (full)
+ * or when the oldest queued request has waited max_delay_us. */
+typedef struct hstu_batcher hstu_batcher;
+typedef struct {
+  int32_t max_batch;     /* >= 1 */
+  int64_t max_delay_us;  /* >= 0 */
+  int64_t max_tokens;    /* >= 0, 0 = no token budget */
+} hstu_batcher_desc;
+
+hstu_status hstu_batcher_create(const hstu_batcher_desc *desc, hstu_batcher **out);
+hstu_status hstu_batcher_destroy(hstu_batcher *batcher);
+/* Queues one request (n_new >= 0). */
+hstu_status hstu_batcher_submit(hstu_batcher *batcher, int64_t request_id, int64_t user, int32_t n_new,
+                                int64_t arrival_us);
+/* At time now_us: if a batch is released, its request ids (host out, capacity
+ * cap, batch order = submission order) and *n = its size, *wait_us = 0; they
+ * leave the queue.  Otherwise *n = 0 and *wait_us = the time until the oldest
+ * request's delay runs out (-1: queue empty).  INVALID (queue unchanged) if
+ * cap is smaller than the released batch. */
+hstu_status hstu_batcher_next(hstu_batcher *batcher, int64_t now_us, int64_t *request_ids, int32_t cap,
+                              int32_t *n, int64_t *wait_us);
+/* *n = queued requests. */
+hstu_status hstu_batcher_pending(const hstu_batcher *batcher, int32_t *n);
+
+/* ======================================================================== */
 /* Instrumentation: kernel durations measured with HIP events               */
 /* ======================================================================== */
 

@@ -1,0 +1,111 @@
+"""GPU checks of the serving loop (dynamic batching with host cache work
+overlapped with the previous batch's kernels): two batches in flight give
+bit-identical logits to one at a time on the same arrivals, and sampled
+requests match the oracle's full recompute of the user's whole sequence plus
+the head, with and without a host tier."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from generative_recommender_sequence_amd import runtime, serving
+from generative_recommender_sequence_amd.workloads import (Config, HEAD_HIDDEN, HEAD_TASKS, generate,
+                                                            head_weights, small_config)
+from gpu_checks import rel, say
+
+pytestmark = pytest.mark.gpu
+
+T = 16
+CFG = Config("serve-small", "bf16", 4, 256, 2, 128, 2, ("lognormal", 150, 16, 300), T, "mixed", page_size=32)
+MAX_BATCH, USERS = 4, 24
+TOL_SERVE = 5e-2   # bf16 Y and K/V storage through two layers, then the head
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    runtime.require_gpu()
+
+
+def _layers():
+    w = generate(small_config(dtype="bf16", num_heads=2, head_dim=128, num_layers=2, n_targets=T), 11,
+                 batch=1, hist_override=[1])
+    for lw in w.layers:
+        lw.w1 *= 4.0
+        lw.w2 *= 4.0
+    return w.layers
+
+
+def _serve(pop0, arrivals, depth, host_pages=0):
+    pop = copy.deepcopy(pop0)
+    pages = sum(-(-(int(h) + 6 + T) // CFG.page_size) for h in pop.hist) // 2
+    pages = max(pages, MAX_BATCH * (-(-(300 + 6 + T) // CFG.page_size)))
+    srv = serving.Server(CFG, _layers(), pop, pages, host_pages=host_pages, max_batch=MAX_BATCH, depth=depth,
+                         max_delay_us=200)
+    log, keep = [], {}
+    srv.on_launch = lambda *a: log.append(a)
+    stats = srv.run(arrivals, keep_logits=keep)
+    return srv, log, keep, stats
+
+
+def _sequences(srv, log):
+    """Each request's whole input sequence (history then candidates),
+    rebuilt from the launches: the request's new tokens are the first rows of
+    the input pool; a miss replaces the user's history, a hit extends it."""
+    x = srv.x.float().cpu().numpy().astype(np.float64)
+    hist_rows, seqs = {}, {}
+    for ids, users, cached, hist, new_len in log:
+        off = np.concatenate([[0], np.cumsum(new_len)])
+        for b, (rid, u) in enumerate(zip(ids, users)):
+            rows = x[off[b]:off[b + 1]]
+            n_hist_new = int(new_len[b]) - T
+            prev = hist_rows.get(int(u), np.zeros((0, x.shape[1])))
+            assert int(cached[b]) in (0, len(prev))
+            hist_rows[int(u)] = np.concatenate([prev[:int(cached[b])], rows[:n_hist_new]])
+            assert len(hist_rows[int(u)]) == int(hist[b])
+            seqs[rid] = (np.concatenate([hist_rows[int(u)], rows[n_hist_new:]]), int(hist[b]))
+    return seqs
+
+
+def _check_oracle(srv, log, keep, n_check, label):
+    seqs = _sequences(srv, log)
+    layers = _layers()
+    hw = head_weights(CFG.d_model, HEAD_TASKS, HEAD_HIDDEN, 0, CFG.dtype)
+    worst = 0.0
+    for rid in sorted(seqs)[-n_check:]:
+        seq, h = seqs[rid]
+        y = oracle.stack(layers, [seq], [T], [h + T], CFG.num_heads, CFG.head_dim, CFG.eps)[0]
+        ref = oracle.head(y, np.arange(len(y) - T, len(y)), hw.a, hw.b, hw.w, hw.c)
+        worst = max(worst, rel(keep[rid].astype(np.float64), ref))
+    say(f"  {label}: {n_check} requests vs oracle, worst rel err {worst:.2e}")
+    assert worst < TOL_SERVE
+
+
+def test_overlap_is_exact_and_matches_oracle():
+    rng = np.random.default_rng(2)
+    pop0 = serving.Population.draw(rng, USERS, CFG, events=(0, 6))
+    arrivals = serving.poisson_arrivals(rng, pop0, float("inf"), 96)
+    srv1, log1, keep1, st1 = _serve(pop0, arrivals, depth=1)
+    srv2, log2, keep2, st2 = _serve(pop0, arrivals, depth=2)
+    say(f"serving: depth 1 {st1.summary()}")
+    say(f"serving: depth 2 {st2.summary()}")
+    assert [l[0] for l in log1] == [l[0] for l in log2]          # the same batches
+    assert sorted(keep1) == list(range(len(arrivals))) == sorted(keep2)
+    for rid in keep1:
+        assert np.array_equal(keep1[rid], keep2[rid]), rid
+    s = st2.summary()
+    assert 0.0 < s["hit_rate"] < 1.0                             # hits, and misses after eviction
+    _check_oracle(srv2, log2, keep2, 10, "device cache")
+
+
+def test_host_tier_serving_matches_oracle():
+    rng = np.random.default_rng(3)
+    pop0 = serving.Population.draw(rng, USERS, CFG, events=(0, 6))
+    arrivals = serving.poisson_arrivals(rng, pop0, float("inf"), 96)
+    host_pages = 2 * sum(-(-(int(h) + 6 * 96 + T) // CFG.page_size) for h in pop0.hist)
+    srv, log, keep, st = _serve(pop0, arrivals, depth=2, host_pages=host_pages)
+    s = st.summary()
+    say(f"serving with host tier: {s}")
+    assert s["onboarded"] > 0
+    _check_oracle(srv, log, keep, 10, "host tier")
