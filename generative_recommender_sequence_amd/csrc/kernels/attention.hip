@@ -22,13 +22,15 @@
 //   K and V tiles are staged row-major in LDS (16-byte-chunk XOR swizzles);
 //   the V operand is read with ds_read_b64_tr_b16, which hands each lane 4
 //   consecutive keys of one column, so V is never transposed in registers.
-//   The next tile's K/V rows are fetched into registers while the current
-//   tile is multiplied, and the work item's page-table slice is staged in LDS
-//   once, so no tile waits on a dependent page-table load.  The bias of a tile
-//   comes from a reversed per-tile table in LDS read with immediate offsets,
-//   or from one scalar when a wave's distance range falls in a single bucket.
-//   Masking work is only done on tiles that touch the diagonal or the
-//   candidate block.
+//   The tiles are double-buffered and filled by direct global -> LDS copies
+//   (no register staging): the next visible tile's copy is issued before the
+//   current tile's MFMAs, and each tile costs one barrier.  The work item's
+//   page-table slice is staged in LDS once (the first tile is addressed from
+//   the table itself, so its copy goes out with the set-up loads).  The bias
+//   of a tile comes from one scalar when a wave's distance range falls in a
+//   single bucket, otherwise from a reversed per-tile table in LDS read with
+//   immediate offsets, built only for tiles that need it.  Masking work is
+//   only done on tiles that touch the diagonal or the candidate block.
 #include "common.h"
 
 namespace hstu {

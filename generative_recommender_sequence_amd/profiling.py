@@ -21,7 +21,8 @@ it, giving HBM bytes per dispatch.
 reads: the workload, the grid of its timed attention launch (the attention
 grid with the most dispatches), the calibrated FETCH_SIZE and WRITE_SIZE bytes
 per launch, and a hash of the sources that decide what that launch reads and
-writes.  The benchmark reports the figure only while the hash still matches.
+writes (code only: comments and whitespace are ignored).  The benchmark
+reports the figure only while the hash still matches.
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,11 +42,19 @@ TRAFFIC_SOURCES = ("csrc/kernels/attention.hip", "csrc/kernels/common.h", "csrc/
 TRAFFIC_TABLE = os.path.join(os.path.dirname(_PKG), "profiles", "attention_traffic.txt")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace (a comment edit does not
+    change what a launch reads or writes)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def sources_hash() -> str:
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(_PKG, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(_PKG, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
