@@ -78,6 +78,9 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     lib.oracle_layer.restype = ctypes.c_int
     lib.oracle_layer.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_double] + [i64p] * 3 + [f64p] +
                                  [f64p] + [f32p] * 3 + [ctypes.c_int, i64p, f64p, f64p] + [f64p] * 8)
+    lib.oracle_layer_backward.restype = ctypes.c_int
+    lib.oracle_layer_backward.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_double, i64p, i64p, f64p] + [f64p] * 4 +
+                                          [ctypes.c_int] + [f64p] * 5)
     lib.oracle_head.restype = ctypes.c_int
     lib.oracle_head.argtypes = [f64p, ctypes.c_int64, ctypes.c_int, i32p, ctypes.c_int64, ctypes.c_int,
                                 ctypes.c_int] + [f64p] * 5
@@ -212,6 +215,27 @@ def layer(x, w1, w2, rab, new_len, start, n_targets, norm_n, hist_k, hist_v, num
                           *[_p(out[n], ctypes.c_double) for n in ("xhat", "u", "v", "q", "k", "o", "g", "y")])
     if rc != OK:
         raise ValueError(f"oracle_layer rc={rc}")
+    return out
+
+
+def layer_backward(x, w1, w2, rab, lengths, n_targets, norm_n, dy, num_heads, head_dim, eps=1e-5,
+                   mutant: int = 0) -> Dict[str, np.ndarray]:
+    """Gradients of one layer (every position computed, no cache) for
+    dL/dY = dy: {"x", "w1", "w2", "rab"} in float64 (see
+    oracle_layer_backward in hstu_oracle.c)."""
+    x, w1, w2, rab, dy = (_f64(t) for t in (x, w1, w2, rab, dy))
+    q_off = offsets(lengths)
+    nt = _i64(n_targets)
+    nn = _f64(norm_n)
+    d = x.shape[1]
+    out = {"x": np.zeros_like(x), "w1": np.zeros_like(w1), "w2": np.zeros_like(w2), "rab": np.zeros_like(rab)}
+    rc = load(mutant).oracle_layer_backward(
+        len(lengths), d, num_heads, head_dim, float(eps), _p(q_off, ctypes.c_int64), _p(nt, ctypes.c_int64),
+        _p(nn, ctypes.c_double), _p(x, ctypes.c_double), _p(w1, ctypes.c_double), _p(w2, ctypes.c_double),
+        _p(rab, ctypes.c_double), len(rab), _p(dy, ctypes.c_double), _p(out["x"], ctypes.c_double),
+        _p(out["w1"], ctypes.c_double), _p(out["w2"], ctypes.c_double), _p(out["rab"], ctypes.c_double))
+    if rc != OK:
+        raise ValueError(f"oracle_layer_backward: status {rc}")
     return out
 
 

@@ -370,3 +370,203 @@ int oracle_head(const double *y, int64_t y_rows, int d, const int32_t *rows, int
   }
   return OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* backward of one HSTU layer (training: every position of every user is    */
+/* computed; no cache)                                                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Gradients of a scalar loss with dL/dY = dy, by the chain rule through the
+ * forward above ("How Generative Recommenders Are Redefining RecSys at
+ * Scale", section HSTU support: HSTU training; the forward equations as in
+ * oracle_layer):
+ *   dW2 = g^T dy,  dg = dy W2^T,  dU = dg * LN(o),  dLN(o) = dg * U
+ *   do  = LN'(o) applied to dLN(o):  rstd (dz - mean(dz) - z mean(dz z))
+ *   per visible pair (i, j) of a user and head, z = q_i.k_j + rab[b(i-j)]:
+ *     dP = do_i . v_j / n,  dv_j += SiLU(z) do_i / n,
+ *     dz = dP SiLU'(z) with SiLU'(z) = s(z) (1 + z (1 - s(z))), s = sigmoid,
+ *     dq_i += dz k_j,  dk_j += dz q_i,  drab[b(i-j)] += dz
+ *   da = [dU|dV|dQ|dK],  ds = da * SiLU'(x^ W1),  dW1 = x^T ds
+ *   dx = LN'(x) applied to ds W1^T, plus dy (the residual)
+ * Inputs in double: x [N][d], w1 [d][4 inner], w2 [inner][d], rab [nb],
+ * dy [N][d]; users' rows by q_off, positions 0.. (start = 0).
+ * Outputs: dx [N][d], dw1 [d][4 inner], dw2 [inner][d], drab [nb].
+ */
+static double sigm(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+static double silu_grad(double z) {
+  double s = sigm(z);
+#if ORACLE_MUTANT == 17
+  return s; /* planted: SiLU' taken as the sigmoid */
+#else
+  return s * (1.0 + z * (1.0 - s));
+#endif
+}
+
+/* dx = rstd (dyv - mean(dyv) - yv mean(dyv yv)) for y = LayerNorm(x) = (x - mu) rstd */
+static void ln_backward(const double *yv, const double *dyv, int n, double rstd, double *dxv) {
+  double m1 = 0.0, m2 = 0.0;
+  for (int c = 0; c < n; ++c) {
+    m1 += dyv[c];
+    m2 += dyv[c] * yv[c];
+  }
+  m1 /= n;
+  m2 /= n;
+  for (int c = 0; c < n; ++c) {
+#if ORACLE_MUTANT == 18
+    dxv[c] = rstd * (dyv[c] - yv[c] * m2); /* planted: the mean term dropped */
+#else
+    dxv[c] = rstd * (dyv[c] - m1 - yv[c] * m2);
+#endif
+  }
+}
+
+static double row_ln(const double *x, int n, double eps, double *y) {
+  double mu = 0.0, var = 0.0;
+  for (int c = 0; c < n; ++c) mu += x[c];
+  mu /= n;
+  for (int c = 0; c < n; ++c) var += (x[c] - mu) * (x[c] - mu);
+  var /= n;
+  double rstd = 1.0 / sqrt(var + eps);
+  for (int c = 0; c < n; ++c) y[c] = (x[c] - mu) * rstd;
+  return rstd;
+}
+
+int oracle_layer_backward(int B, int d, int H, int dh, double eps, const int64_t *q_off,
+                          const int64_t *n_targets, const double *norm_n, const double *x,
+                          const double *w1, const double *w2, const double *rab, int num_buckets,
+                          const double *dy, double *dx, double *dw1, double *dw2, double *drab) {
+  if (B < 0 || d <= 0 || H <= 0 || dh <= 0 || num_buckets <= 0) return ERR_INVALID;
+  for (int u = 0; u < B; ++u) {
+    int64_t L = q_off[u + 1] - q_off[u];
+    if (L < 0 || n_targets[u] < 0 || n_targets[u] > L) return ERR_INVALID;
+  }
+  const int inner = H * dh, w = 4 * inner;
+  const int64_t N = q_off[B];
+  size_t nd = (size_t)(N * d + 1), nw = (size_t)(N * w + 1), ni = (size_t)(N * inner + 1);
+  double *xh = calloc(nd, sizeof(double)), *xr = calloc((size_t)N + 1, sizeof(double));
+  double *z1 = calloc(nw, sizeof(double)), *a = calloc(nw, sizeof(double));
+  double *o = calloc(ni, sizeof(double)), *lo = calloc(ni, sizeof(double));
+  double *orr = calloc((size_t)N + 1, sizeof(double)), *g = calloc(ni, sizeof(double));
+  double *dg = calloc(ni, sizeof(double)), *dov = calloc(ni, sizeof(double));
+  double *da = calloc(nw, sizeof(double)), *dxh = calloc(nd, sizeof(double));
+  if (!xh || !xr || !z1 || !a || !o || !lo || !orr || !g || !dg || !dov || !da || !dxh) return ERR_INVALID;
+
+  /* forward, keeping what the backward needs */
+  for (int64_t r = 0; r < N; ++r) xr[r] = row_ln(x + r * d, d, eps, xh + r * d);
+  for (int64_t r = 0; r < N; ++r)
+    for (int c = 0; c < w; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < d; ++k) s += xh[r * d + k] * w1[(int64_t)k * w + c];
+      z1[r * w + c] = s;
+      a[r * w + c] = s * sigm(s);
+    }
+  for (int u = 0; u < B; ++u) {
+    int64_t r0 = q_off[u], L = q_off[u + 1] - r0, hist = L - n_targets[u];
+    for (int h = 0; h < H; ++h)
+      for (int64_t i = 0; i < L; ++i) {
+        const double *qi = a + (r0 + i) * w + 2 * inner + h * dh;
+        double *oi = o + (r0 + i) * inner + h * dh;
+        for (int64_t j = 0; j < L; ++j) {
+          if (!visible(i, j, hist)) continue;
+          const double *kj = a + (r0 + j) * w + 3 * inner + h * dh;
+          const double *vj = a + (r0 + j) * w + 1 * inner + h * dh;
+          double z = rab[oracle_bucket(i - j, num_buckets)];
+          for (int e = 0; e < dh; ++e) z += qi[e] * kj[e];
+          double p = z * sigm(z) / norm_n[u];
+          for (int e = 0; e < dh; ++e) oi[e] += p * vj[e];
+        }
+      }
+  }
+  for (int64_t r = 0; r < N; ++r) {
+    orr[r] = row_ln(o + r * inner, inner, eps, lo + r * inner);
+    for (int c = 0; c < inner; ++c) g[r * inner + c] = lo[r * inner + c] * a[r * w + c];
+  }
+
+  /* f2 and the gate */
+  for (int c = 0; c < inner; ++c)
+    for (int k = 0; k < d; ++k) {
+      double s = 0.0;
+      for (int64_t r = 0; r < N; ++r) s += g[r * inner + c] * dy[r * d + k];
+      dw2[(int64_t)c * d + k] = s;
+    }
+  for (int64_t r = 0; r < N; ++r) {
+    for (int c = 0; c < inner; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < d; ++k) s += dy[r * d + k] * w2[(int64_t)c * d + k];
+      dg[r * inner + c] = s;
+      da[r * w + c] = s * lo[r * inner + c];            /* dU */
+    }
+    double dln[inner];
+    for (int c = 0; c < inner; ++c) dln[c] = dg[r * inner + c] * a[r * w + c];
+    ln_backward(lo + r * inner, dln, inner, orr[r], dov + r * inner);
+  }
+
+  /* attention */
+  for (int b = 0; b < num_buckets; ++b) drab[b] = 0.0;
+  for (int u = 0; u < B; ++u) {
+    int64_t r0 = q_off[u], L = q_off[u + 1] - r0, hist = L - n_targets[u];
+    double n = norm_n[u];
+    for (int h = 0; h < H; ++h)
+      for (int64_t i = 0; i < L; ++i) {
+        const double *qi = a + (r0 + i) * w + 2 * inner + h * dh;
+        const double *doi = dov + (r0 + i) * inner + h * dh;
+        double *dqi = da + (r0 + i) * w + 2 * inner + h * dh;
+        for (int64_t j = 0; j < L; ++j) {
+          if (!visible(i, j, hist)) continue;
+          const double *kj = a + (r0 + j) * w + 3 * inner + h * dh;
+          const double *vj = a + (r0 + j) * w + 1 * inner + h * dh;
+          double *dkj = da + (r0 + j) * w + 3 * inner + h * dh;
+          double *dvj = da + (r0 + j) * w + 1 * inner + h * dh;
+          int bk = oracle_bucket(i - j, num_buckets);
+          double z = rab[bk], dp = 0.0;
+          for (int e = 0; e < dh; ++e) {
+            z += qi[e] * kj[e];
+            dp += doi[e] * vj[e];
+          }
+          dp /= n;
+          double p = z * sigm(z);
+#if ORACLE_MUTANT == 20
+          for (int e = 0; e < dh; ++e) dvj[e] += p * doi[e]; /* planted: 1/n dropped in dV */
+#else
+          for (int e = 0; e < dh; ++e) dvj[e] += p * doi[e] / n;
+#endif
+          double dz = dp * silu_grad(z);
+          for (int e = 0; e < dh; ++e) {
+            dqi[e] += dz * kj[e];
+            dkj[e] += dz * qi[e];
+          }
+#if ORACLE_MUTANT == 19
+          drab[oracle_bucket(i - j + 1, num_buckets)] += dz; /* planted: bias gradient to the wrong bucket */
+#else
+          drab[bk] += dz;
+#endif
+        }
+      }
+  }
+
+  /* f1 and the pre-norm */
+  for (int64_t r = 0; r < N; ++r)
+    for (int c = 0; c < w; ++c) da[r * w + c] *= silu_grad(z1[r * w + c]);
+  for (int k = 0; k < d; ++k)
+    for (int c = 0; c < w; ++c) {
+      double s = 0.0;
+      for (int64_t r = 0; r < N; ++r) s += xh[r * d + k] * da[r * w + c];
+      dw1[(int64_t)k * w + c] = s;
+    }
+  for (int64_t r = 0; r < N; ++r) {
+    for (int k = 0; k < d; ++k) {
+      double s = 0.0;
+      for (int c = 0; c < w; ++c) s += da[r * w + c] * w1[(int64_t)k * w + c];
+      dxh[r * d + k] = s;
+    }
+    ln_backward(xh + r * d, dxh + r * d, d, xr[r], dx + r * d);
+#if ORACLE_MUTANT != 21
+    for (int k = 0; k < d; ++k) dx[r * d + k] += dy[r * d + k];
+#endif
+    /* (mutant 21, planted: the residual's gradient dropped) */
+  }
+  free(xh); free(xr); free(z1); free(a); free(o); free(lo); free(orr); free(g);
+  free(dg); free(dov); free(da); free(dxh);
+  return OK;
+}

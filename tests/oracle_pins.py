@@ -1,7 +1,7 @@
 """Pins of the CPU oracle against things other than itself.
 
 Each pin returns (ok, detail) for a given oracle build (mutant 0 = the real
-oracle; mutants 1..16 each plant one deliberate mistake, see hstu_oracle.c).
+oracle; mutants 1..21 each plant one deliberate mistake, see hstu_oracle.c).
 test_oracle.py asserts that the real oracle passes every pin and that every
 mutant fails at least one, so a plausible slip anywhere in the oracle (a wrong
 sign, a dropped term, an index off by one, a transposed operand, swapped
@@ -23,6 +23,9 @@ What pins what:
               move when future tokens change; a candidate's input moves only
               its own rows; cached prefix + append equals full recompute
               bit for bit; a jagged batch equals each user run alone
+  backward    every gradient entry (x, W1, W2, rab) of a small jagged layer
+              with candidates against central differences of the brute
+              force's loss sum(dY * Y)
   head        torch.nn Linear -> ReLU -> Linear per task (float64); the
               affine closed form when every hidden unit is active and the
               output bias alone when none is; the row list against scoring
@@ -291,6 +294,50 @@ def pin_head_rows(m=0):
     return bool(np.array_equal(got, singles)), "row gather"
 
 
+def _bwd_case(seed):
+    rng = np.random.default_rng(seed)
+    lengths, n_targets, norm_n = [5, 7], [2, 0], [5.5, 7.0]
+    d, H, dh, nb = 8, 2, 4, 16
+    inner = H * dh
+    n = sum(lengths)
+    return dict(x=rng.standard_normal((n, d)), w1=rng.standard_normal((d, 4 * inner)) * 0.5,
+                w2=rng.standard_normal((inner, d)) * 0.5, rab=rng.standard_normal(nb) * 0.5,
+                dy=rng.standard_normal((n, d)), lengths=lengths, n_targets=n_targets, norm_n=norm_n,
+                H=H, dh=dh)
+
+
+def _brute_loss(c, x, w1, w2, rab):
+    """sum(dy * Y) with Y from the dense float64 brute force."""
+    L = max(c["lengths"])
+    off = np.concatenate([[0], np.cumsum(c["lengths"])])
+    xp = np.zeros((len(c["lengths"]), L, x.shape[1]))
+    for b in range(len(c["lengths"])):
+        xp[b, :c["lengths"][b]] = x[off[b]:off[b + 1]]
+    y = brute.layer(xp, c["lengths"], c["n_targets"], c["norm_n"], w1, w2, rab, c["H"], c["dh"])["y"]
+    return sum(float(np.sum(y[b, :c["lengths"][b]] * c["dy"][off[b]:off[b + 1]]))
+               for b in range(len(c["lengths"])))
+
+
+def pin_backward_finite_differences(m=0):
+    """Every gradient entry (x, W1, W2, rab) against central differences of
+    the brute-force forward's loss sum(dy * Y), h = 1e-6."""
+    c = _bwd_case(4)
+    got = oracle.layer_backward(c["x"], c["w1"], c["w2"], c["rab"], c["lengths"], c["n_targets"], c["norm_n"],
+                                c["dy"], c["H"], c["dh"], mutant=m)
+    h, worst = 1e-6, 0.0
+    for name in ("x", "w1", "w2", "rab"):
+        fd = np.zeros_like(c[name])
+        for idx in np.ndindex(c[name].shape):
+            args = {k: c[k].copy() for k in ("x", "w1", "w2", "rab")}
+            args[name][idx] += h
+            lp = _brute_loss(c, **args)
+            args[name][idx] -= 2 * h
+            lm = _brute_loss(c, **args)
+            fd[idx] = (lp - lm) / (2 * h)
+        worst = max(worst, _relerr(got[name], fd))
+    return worst < 1e-6, f"backward vs finite differences: worst rel err {worst:.2e}"
+
+
 PINS = [pin_silu, pin_layer_norm, pin_bucket, pin_attention_closed_form, pin_layer_vs_brute,
         pin_c1_vs_brute, pin_identity, pin_causal, pin_target_isolation, pin_cache, pin_jagged,
-        pin_head_torch, pin_head_regimes, pin_head_rows]
+        pin_head_torch, pin_head_regimes, pin_head_rows, pin_backward_finite_differences]

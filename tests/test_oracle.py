@@ -6,7 +6,7 @@ import pytest
 import oracle
 import oracle_pins
 
-N_MUTANTS = 16
+N_MUTANTS = 21
 
 
 @pytest.mark.parametrize("pin", oracle_pins.PINS, ids=lambda f: f.__name__)
