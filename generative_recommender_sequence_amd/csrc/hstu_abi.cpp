@@ -567,6 +567,8 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
     return fail(HSTU_ERR_UNSUPPORTED,
                 "hstu_layer_forward: d_model must be a multiple of 128 (bf16) or 4 (fp32)");
   if (!(a->eps >= 0.f)) return fail(HSTU_ERR_INVALID, "hstu_layer_forward: eps must be >= 0");
+  if (a->s_out && a->dtype != HSTU_BF16)
+    return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_forward: the s_out tap is bf16 only");
   if (p->n_new == 0) return ok();
   if (!a->x || !a->y || !a->w1 || !a->w2 || !a->rab || a->num_buckets <= 0)
     return fail(HSTU_ERR_INVALID, "hstu_layer_forward: null x/y/w1/w2/rab or no buckets");
@@ -618,7 +620,6 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   }
   const hstu_kv_cache* c = a->cache;
   if (a->dtype == HSTU_BF16) {
-    // row statistics, then f1 with the pre-norm, SiLU and the K/V append fused
     // row records (statistics, page slots) and W1's column sums, then f1 with
     // the pre-norm, SiLU and the K/V append fused
     auto* info = static_cast<RowInfo*>(xhat);
@@ -627,6 +628,7 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
     f.uvqk = uvqk;
     f.inner = inner;
     f.kv_to_uvqk = a->uvqk_out != nullptr;
+    f.s_out = a->s_out;
     f.dh = dh;
     RowPages pg{};
     if (paged) {
@@ -681,6 +683,180 @@ hstu_status hstu_stack_forward(const hstu_layer_args* layers, int32_t n, hipStre
     if (st != HSTU_OK) return fail(st, "hstu_stack_forward: layer " + std::to_string(i) + ": " + g_last_error);
   }
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// backward of one layer
+// ---------------------------------------------------------------------------
+
+namespace {
+struct BwdWs {
+  size_t dg, dout, g, da, dxh, xhat, zeros, part, drab_part, kv_items, q_items, total;
+  int32_t n_kv, n_q, splits1, splits2;
+};
+constexpr int kBwdKeys = 128;  // keys per key-block item
+constexpr int kWgradTile = 128;
+
+int32_t wgrad_splits(int32_t M, int32_t N1, int32_t N2) {
+  const int32_t tiles = (N1 / kWgradTile) * (N2 / kWgradTile);
+  int32_t s = (512 + tiles - 1) / tiles;
+  const int32_t max_s = std::max(1, (M + 63) / 64);
+  return std::max(1, std::min(s, max_s));
+}
+
+BwdWs bwd_ws(const hstu_plan* p, int32_t d) {
+  const size_t n = static_cast<size_t>(p->n_new), inner = p->desc.num_heads * p->desc.head_dim;
+  BwdWs w{};
+  w.n_kv = 0;
+  for (size_t u = 0; u < p->users.size(); ++u)
+    w.n_kv += (p->users[u].kv_len + kBwdKeys - 1) / kBwdKeys * p->desc.num_heads;
+  w.n_q = static_cast<int32_t>(p->qblocks.size()) * p->desc.num_heads;
+  const int32_t M = p->n_new, W = static_cast<int32_t>(4 * inner);
+  w.splits1 = wgrad_splits(M, W, d);
+  w.splits2 = wgrad_splits(M, d, static_cast<int32_t>(inner));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes + 1);
+    return at;
+  };
+  w.dg = take(n * inner * 2);
+  w.dout = take(n * inner * 2);
+  w.g = take(n * inner * 2);
+  w.da = take(n * 4 * inner * 2);
+  w.dxh = take(n * d * 2);
+  w.xhat = take(n * d * 2);
+  w.zeros = take(256 * 2);
+  w.part = take(std::max(static_cast<size_t>(w.splits1) * W * d, static_cast<size_t>(w.splits2) * d * inner) * 4);
+  w.drab_part = take(static_cast<size_t>(w.n_kv) * 256 * 4);
+  w.kv_items = take(static_cast<size_t>(w.n_kv) * sizeof(BwdKVItem));
+  w.q_items = take(static_cast<size_t>(w.n_q) * sizeof(BwdQItem));
+  w.total = off;
+  return w;
+}
+
+hstu_status bwd_check(const hstu_layer_bwd_args* a, const char* who) {
+  if (!a) return fail(HSTU_ERR_INVALID, std::string(who) + ": null args");
+  hstu_status st = check_plan(a->plan, who);
+  if (st != HSTU_OK) return st;
+  const hstu_plan* p = a->plan;
+  if (a->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": bf16 only");
+  if (p->desc.head_dim != 128 || p->desc.num_heads * p->desc.head_dim > 512)
+    return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": head_dim 128 and H*head_dim <= 512 only");
+  if (a->d_model <= 0 || a->d_model % 128 || a->d_model > 2048)
+    return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": d_model must be a multiple of 128, <= 2048");
+  if (p->desc.page_size != 0) return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": paged plans are not supported");
+  for (int32_t c : p->cached_len)
+    if (c != 0) return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": cached positions are not supported");
+  if (a->num_buckets <= 0 || a->num_buckets > 256)
+    return fail(HSTU_ERR_INVALID, std::string(who) + ": num_buckets must be in [1, 256]");
+  if (!(a->eps >= 0.f)) return fail(HSTU_ERR_INVALID, std::string(who) + ": eps must be >= 0");
+  return HSTU_OK;
+}
+}  // namespace
+
+hstu_status hstu_layer_backward_workspace_size(const hstu_layer_bwd_args* a, size_t* bytes) {
+  if (!bytes) return fail(HSTU_ERR_INVALID, "hstu_layer_backward_workspace_size: null output");
+  hstu_status st = bwd_check(a, "hstu_layer_backward_workspace_size");
+  if (st != HSTU_OK) return st;
+  *bytes = bwd_ws(a->plan, a->d_model).total;
+  return ok();
+}
+
+hstu_status hstu_layer_backward(const hstu_layer_bwd_args* a, hipStream_t stream) {
+  hstu_status st = bwd_check(a, "hstu_layer_backward");
+  if (st != HSTU_OK) return st;
+  const hstu_plan* p = a->plan;
+  const int32_t M = p->n_new, d = a->d_model, H = p->desc.num_heads, inner = H * p->desc.head_dim, W = 4 * inner;
+  if (!a->x || !a->w1t || !a->w2t || !a->rab || !a->uvqk || !a->s || !a->o || !a->dy || !a->dx || !a->dw1 ||
+      !a->dw2 || !a->drab)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_backward: null buffer");
+  BwdWs w = bwd_ws(p, d);
+  if (!a->workspace || a->workspace_bytes < w.total)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_backward: workspace too small");
+  if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_backward: workspace must be 256-byte aligned");
+  auto* ws = static_cast<unsigned char*>(a->workspace);
+  void* dg = ws + w.dg;
+  void* dout = ws + w.dout;
+  void* g = ws + w.g;
+  void* da = ws + w.da;
+  void* dxh = ws + w.dxh;
+  void* xhat = ws + w.xhat;
+  void* zeros = ws + w.zeros;
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  float* drab_part = reinterpret_cast<float*>(ws + w.drab_part);
+
+  // work lists: key blocks and query blocks of every (user, head), the
+  // longest first (a key block's work grows with the queries after it)
+  std::vector<BwdKVItem> kv;
+  kv.reserve(static_cast<size_t>(w.n_kv));
+  for (size_t u = 0; u < p->users.size(); ++u)
+    for (int32_t k0 = 0; k0 < p->users[u].kv_len; k0 += kBwdKeys)
+      for (int32_t h = 0; h < H; ++h) kv.push_back(BwdKVItem{static_cast<int32_t>(u), h, k0, 0});
+  std::stable_sort(kv.begin(), kv.end(), [&](const BwdKVItem& x, const BwdKVItem& y) {
+    return p->users[x.user].kv_len - x.k0 > p->users[y.user].kv_len - y.k0;
+  });
+  std::vector<BwdQItem> qi;
+  qi.reserve(static_cast<size_t>(w.n_q));
+  for (size_t q = 0; q < p->qblocks.size(); ++q)
+    for (int32_t h = 0; h < H; ++h) qi.push_back(BwdQItem{static_cast<int32_t>(q), h});
+  std::stable_sort(qi.begin(), qi.end(), [&](const BwdQItem& x, const BwdQItem& y) {
+    return p->qblocks[x.qblock].pos0 + p->qblocks[x.qblock].count >
+           p->qblocks[y.qblock].pos0 + p->qblocks[y.qblock].count;
+  });
+  if (!kv.empty() &&
+      (st = staged_upload(ws + w.kv_items, kv.data(), kv.size() * sizeof(BwdKVItem), stream)) != HSTU_OK)
+    return st;
+  if (!qi.empty() &&
+      (st = staged_upload(ws + w.q_items, qi.data(), qi.size() * sizeof(BwdQItem), stream)) != HSTU_OK)
+    return st;
+
+  const int64_t W64 = W;
+  if ((st = check_hip(launch_fill_zero(zeros, 256, stream), "hstu_layer_backward: zeros")) != HSTU_OK) return st;
+  if (M > 0) {
+    if ((st = check_hip(timed(TK_BWD_GEMM, stream, [&] { return launch_gemm(HSTU_BF16, 3, a->dy, a->w2t, dg, nullptr, M, inner, d, stream); }),
+                        "hstu_layer_backward: dg")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_BWD_ROWS, stream, [&] { return launch_gate_bwd(a->o, a->uvqk, W64, dg, M, inner, a->eps, da, dout, g, stream); }),
+                        "hstu_layer_backward: gate")) != HSTU_OK)
+      return st;
+    BwdLaunch b{};
+    b.plan = p->dev;
+    b.a = static_cast<const uint16_t*>(a->uvqk);
+    b.dO = static_cast<const uint16_t*>(dout);
+    b.da = static_cast<uint16_t*>(da);
+    b.rab = a->rab;
+    b.num_buckets = a->num_buckets;
+    b.drab_partial = drab_part;
+    b.kv_items = reinterpret_cast<const BwdKVItem*>(ws + w.kv_items);
+    b.n_kv_items = static_cast<int32_t>(kv.size());
+    b.q_items = reinterpret_cast<const BwdQItem*>(ws + w.q_items);
+    b.n_q_items = static_cast<int32_t>(qi.size());
+    if ((st = check_hip(timed(TK_BWD_ATTENTION, stream, [&] {
+                          hipError_t e = launch_attn_bwd(b, stream);
+                          return e != hipSuccess ? e : launch_drab_sum(drab_part, b.n_kv_items, a->num_buckets, a->drab, stream);
+                        }),
+                        "hstu_layer_backward: attention")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_BWD_ROWS, stream, [&] { return launch_silu_grad(da, a->s, static_cast<int64_t>(M) * W, stream); }),
+                        "hstu_layer_backward: SiLU'")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_BWD_GEMM, stream, [&] { return launch_gemm(HSTU_BF16, 3, da, a->w1t, dxh, nullptr, M, d, W, stream); }),
+                        "hstu_layer_backward: dx^")) != HSTU_OK)
+      return st;
+    if ((st = check_hip(timed(TK_BWD_ROWS, stream, [&] { return launch_ln_bwd(a->x, dxh, a->dy, M, d, a->eps, a->dx, xhat, stream); }),
+                        "hstu_layer_backward: pre-norm")) != HSTU_OK)
+      return st;
+  } else {
+    if ((st = check_hip(launch_drab_sum(drab_part, 0, a->num_buckets, a->drab, stream), "hstu_layer_backward: drab")) != HSTU_OK)
+      return st;
+  }
+  if ((st = check_hip(timed(TK_BWD_GEMM, stream, [&] { return launch_wgrad(a->dy, d, g, inner, M, d, inner, w.splits2, zeros, part, a->dw2, stream); }),
+                      "hstu_layer_backward: dW2")) != HSTU_OK)
+    return st;
+  return check_hip(timed(TK_BWD_GEMM, stream, [&] { return launch_wgrad(da, W64, xhat, d, M, W, d, w.splits1, zeros, part, a->dw1, stream); }),
+                   "hstu_layer_backward: dW1");
 }
 
 // ---------------------------------------------------------------------------

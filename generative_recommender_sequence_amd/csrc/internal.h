@@ -116,7 +116,8 @@ struct hstu_kv_cache {
 namespace hstu {
 
 // ---- optional event timing of launches (hstu_timing_*) ---------------------
-enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_HEAD, TK_COUNT };
+enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_HEAD,
+                   TK_BWD_ATTENTION, TK_BWD_GEMM, TK_BWD_ROWS, TK_COUNT };
 // Brackets one launch: records a start event now and an end event when the
 // returned guard's end() is called (both on stream s), if timing is enabled.
 struct TimedLaunch {
@@ -224,6 +225,7 @@ struct F1Args {
   void* v_pool;
   int64_t pool_layer_offset;
   int32_t dh, page_size;
+  void* s_out;            // optional [M][4 inner]: the pre-activation LayerNorm(x) . W1
 };
 // [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row stats, routed per F1Args
 hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
@@ -246,5 +248,38 @@ struct HeadArgs {
   float* partial;         // [n_rows][tasks*hidden/kHeadTile] scratch
 };
 hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s);
+
+// ---- backward (training; contiguous keys, every position computed) ----
+struct BwdKVItem {
+  int32_t user, head, k0, pad;  // 128 keys from position k0
+};
+struct BwdQItem {
+  int32_t qblock, head;
+};
+struct BwdLaunch {
+  PlanDev plan;
+  const uint16_t* a;      // [N][4 inner] post-SiLU [U|V|Q|K]
+  const uint16_t* dO;     // [N][inner] gradient of o (o includes 1/n)
+  uint16_t* da;           // [N][4 inner]: the attention writes the V, Q and K chunks
+  const float* rab;
+  int32_t num_buckets;
+  float* drab_partial;    // [n_kv_items][num_buckets]
+  const BwdKVItem* kv_items;
+  int32_t n_kv_items;
+  const BwdQItem* q_items;
+  int32_t n_q_items;
+};
+hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s);
+hipError_t launch_drab_sum(const float* part, int32_t items, int32_t nb, float* drab, hipStream_t s);
+hipError_t launch_gate_bwd(const float* o, const void* a, int64_t a_stride, const void* dg, int32_t rows,
+                           int32_t inner, float eps, void* du, void* dout, void* g, hipStream_t s);
+hipError_t launch_ln_bwd(const void* x, const void* dxh, const void* dy, int32_t rows, int32_t d, float eps,
+                         void* dx, void* xhat, hipStream_t s);
+hipError_t launch_silu_grad(void* da, const void* s_pre, int64_t n, hipStream_t s);
+hipError_t launch_fill_zero(void* p, int32_t n, hipStream_t s);
+// out[i][j] = sum_m A[m][i] B[m][j] (fp32), split over m into `splits` chunks
+// whose partials [splits][N1][N2] go to `part`; rows past M read `zeros`
+hipError_t launch_wgrad(const void* A, int64_t lda, const void* B, int64_t ldb, int32_t M, int32_t N1, int32_t N2,
+                        int32_t splits, const void* zeros, float* part, float* out, hipStream_t s);
 
 }  // namespace hstu

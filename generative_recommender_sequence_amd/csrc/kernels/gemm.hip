@@ -67,6 +67,7 @@ struct F1Route {
   const float* h_bias;        // [N] hidden bias
   const float* h_wout;        // [N] output weights
   float* h_partial;           // [M][N / BN] partial logits
+  uint16_t* s_out;            // epilogue 0: the pre-activation x^ W1 [M][N] (nullptr: not kept)
 };
 
 template <int BM, int BN, int EPI>
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.colsum[n0 + 4 * tid]);
 #pragma unroll
     for (int i = 0; i < MT; ++i) rinfo[i] = route.rows[min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1)];
-  } else {
+  } else if (EPI == 1) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int m = min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1);
@@ -257,17 +258,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = nb + 8 * q + 4 * g;  // first of this lane's 4 columns
-        float v[4];
+        float v[4], z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
         if (EPI == 0) {
           const f32x4 cs = *reinterpret_cast<const f32x4*>(&cs_lds[n - n0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float z = rstd * (v[e] - mu * cs[e]);
-            v[e] = z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896340736f));
+            z[e] = rstd * (v[e] - mu * cs[e]);
+            v[e] = z[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[e] * -1.44269504088896340736f));
           }
-        } else {
+        } else if (EPI == 1) {
           const u32x2 r2 = resid[i][j][q];
           v[0] += bf2f(r2[0] & 0xFFFFu);
           v[1] += bf2f(r2[0] >> 16);
@@ -276,9 +277,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
         }
         const u32x2 packed = {uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16),
                               uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
-        if (EPI == 1) {
+        if (EPI == 1 || EPI == 3) {
           *reinterpret_cast<u32x2*>(C + static_cast<int64_t>(m) * N + n) = packed;
           continue;
+        }
+        if (EPI == 0 && route.s_out) {  // pre-activation tap (f1)
+          const u32x2 pre = {uint32_t(f2bf(z[0])) | (uint32_t(f2bf(z[1])) << 16),
+                             uint32_t(f2bf(z[2])) | (uint32_t(f2bf(z[3])) << 16)};
+          *reinterpret_cast<u32x2*>(route.s_out + static_cast<int64_t>(m) * N + n) = pre;
         }
         if (to_uvqk) *reinterpret_cast<u32x2*>(route.uvqk + static_cast<int64_t>(m) * N + n) = packed;
         if (to_pool) {
@@ -459,6 +465,7 @@ hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsu
   r.pool_layer_offset = f.pool_layer_offset;
   r.dh = f.dh;
   r.page_size = f.page_size;
+  r.s_out = static_cast<uint16_t*>(f.s_out);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1t),
                      static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
@@ -496,13 +503,19 @@ hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, v
                        const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (dtype == HSTU_BF16) {
-    // the bf16 path only uses this for f2 (+ residual); f1 goes through launch_f1_bf16
+    // bf16: f2 (+ residual, epilogue 1) and the backward's plain products
+    // (epilogue 3); f1 goes through launch_f1_bf16
     constexpr int BM = 64, BN = 128;
-    if (epilogue != 1 || N % BN != 0 || K % GBK != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
-                       static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), F1Route{}, M, N,
-                       K);
+    if ((epilogue != 1 && epilogue != 3) || N % BN != 0 || K % GBK != 0) return hipErrorInvalidValue;
+    if (epilogue == 1)
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                         static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), F1Route{}, M, N,
+                         K);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 3>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                         static_cast<uint16_t*>(C), nullptr, F1Route{}, M, N, K);
   } else {
     dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT);
     auto a = static_cast<const float*>(A);

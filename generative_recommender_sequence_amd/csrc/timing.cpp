@@ -11,7 +11,8 @@ namespace hstu {
 namespace {
 
 const char* kNames[TK_COUNT] = {"layer_norm", "f1_gemm",  "append", "attention",
-                                "reduce_gate", "f2_gemm", "gather", "head"};
+                                "reduce_gate", "f2_gemm", "gather", "head",
+                                "bwd_attention", "bwd_gemm", "bwd_rows"};
 
 struct TimingState {
   std::mutex mu;

@@ -58,7 +58,15 @@ class hstu_layer_args(ctypes.Structure):
     _fields_ = [("dtype", c_i32), ("d_model", c_i32), ("eps", c_f32), ("plan", c_vp), ("x", c_vp),
                 ("y", c_vp), ("w1", c_vp), ("w2", c_vp), ("rab", c_vp), ("num_buckets", c_i32),
                 ("cache", c_vp), ("layer", c_i32), ("d_page_table", c_vp), ("workspace", c_vp),
-                ("workspace_bytes", c_size), ("uvqk_out", c_vp), ("o_out", c_vp), ("g_out", c_vp)]
+                ("workspace_bytes", c_size), ("uvqk_out", c_vp), ("o_out", c_vp), ("g_out", c_vp),
+                ("s_out", c_vp)]
+
+
+class hstu_layer_bwd_args(ctypes.Structure):
+    _fields_ = [("dtype", c_i32), ("d_model", c_i32), ("eps", c_f32), ("plan", c_vp), ("x", c_vp),
+                ("w1t", c_vp), ("w2t", c_vp), ("rab", c_vp), ("num_buckets", c_i32), ("uvqk", c_vp), ("s", c_vp),
+                ("o", c_vp), ("dy", c_vp), ("dx", c_vp), ("dw1", c_vp), ("dw2", c_vp), ("drab", c_vp),
+                ("workspace", c_vp), ("workspace_bytes", c_size)]
 
 
 class hstu_head_args(ctypes.Structure):
@@ -101,6 +109,8 @@ SIGNATURES = {
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
     "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
+    "hstu_layer_backward_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_bwd_args), ctypes.POINTER(c_size)]),
+    "hstu_layer_backward": (c_i32, [ctypes.POINTER(hstu_layer_bwd_args), c_vp]),
     "hstu_head_workspace_size": (c_i32, [ctypes.POINTER(hstu_head_args), ctypes.POINTER(c_size)]),
     "hstu_head_forward": (c_i32, [ctypes.POINTER(hstu_head_args), c_vp]),
     "hstu_batcher_create": (c_i32, [ctypes.POINTER(hstu_batcher_desc), ctypes.POINTER(c_vp)]),
@@ -112,7 +122,8 @@ SIGNATURES = {
     "hstu_timing_read": (c_i32, [ctypes.c_char_p, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
 
-TIMED_KERNELS = ("layer_norm", "f1_gemm", "append", "attention", "reduce_gate", "f2_gemm", "gather", "head")
+TIMED_KERNELS = ("layer_norm", "f1_gemm", "append", "attention", "reduce_gate", "f2_gemm", "gather", "head",
+                 "bwd_attention", "bwd_gemm", "bwd_rows")
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -411,6 +422,17 @@ def hstu_stack_forward(layers, stream: int):
     else:
         arr = layers
     _check(lib().hstu_stack_forward(arr, len(arr), stream), "hstu_stack_forward")
+
+
+def hstu_layer_backward_workspace_size(args: hstu_layer_bwd_args) -> int:
+    n = c_size(0)
+    _check(lib().hstu_layer_backward_workspace_size(ctypes.byref(args), ctypes.byref(n)),
+           "hstu_layer_backward_workspace_size")
+    return n.value
+
+
+def hstu_layer_backward(args: hstu_layer_bwd_args, stream: int):
+    _check(lib().hstu_layer_backward(ctypes.byref(args), stream or None), "hstu_layer_backward")
 
 
 def hstu_head_workspace_size(args: hstu_head_args) -> int:

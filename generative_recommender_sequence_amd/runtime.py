@@ -53,6 +53,9 @@ class Model:
         self.w1 = [torch.from_numpy(np.ascontiguousarray(lw.w1.T)).to(device=device, dtype=t) for lw in layers]
         self.w2 = [torch.from_numpy(np.ascontiguousarray(lw.w2.T)).to(device=device, dtype=t) for lw in layers]
         self.rab = [torch.from_numpy(np.ascontiguousarray(lw.rab, dtype=np.float32)).to(device) for lw in layers]
+        # W1 [d][4 H dh] and W2 [H dh][d] in the layout of x . W1 and g . W2 (the backward's operands)
+        self.w1t = [w.t().contiguous() for w in self.w1]
+        self.w2t = [w.t().contiguous() for w in self.w2]
 
     @property
     def num_layers(self) -> int:
@@ -237,6 +240,7 @@ def layer_args(model: Model, req: Request, li: int, x: torch.Tensor, y: torch.Te
         a.uvqk_out = taps["uvqk"].data_ptr() if "uvqk" in taps else None
         a.o_out = taps["o"].data_ptr() if "o" in taps else None
         a.g_out = taps["g"].data_ptr() if "g" in taps else None
+        a.s_out = taps["s"].data_ptr() if "s" in taps else None
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel()
@@ -270,6 +274,57 @@ def forward(model: Model, req: Request, x: torch.Tensor, cache: Optional[PagedCa
         cur = out
     hstu.hstu_stack_forward(args, s)
     return cur
+
+
+def forward_for_backward(model: Model, req: Request, x: torch.Tensor, stream=None):
+    """The stack on x (contiguous keys, no cache), one layer at a time,
+    keeping what the backward reuses: per layer its input and the uvqk, s
+    and o taps.  Returns (y, saved)."""
+    inner = model.num_heads * model.head_dim
+    n = x.shape[0]
+    t = tdtype(model.dtype)
+    ws = workspace_for(model, req, x.device)
+    saved, cur = [], x
+    for li in range(model.num_layers):
+        taps = {"uvqk": torch.empty((n, 4 * inner), dtype=t, device=x.device),
+                "s": torch.empty((n, 4 * inner), dtype=t, device=x.device),
+                "o": torch.empty((n, inner), dtype=torch.float32, device=x.device)}
+        y = forward(model, req, cur, None, ws, layers=[li], taps=[taps], stream=stream,
+                    out_bufs=[torch.empty_like(cur)])
+        saved.append(dict(x=cur, **taps))
+        cur = y
+    return cur, saved
+
+
+def backward(model: Model, req: Request, saved, dy: torch.Tensor, stream=None,
+             workspace: Optional[torch.Tensor] = None, stop_at: int = 0):
+    """hstu_layer_backward from the last layer down to layer stop_at.  Returns
+    (dL/d(input of layer stop_at), per-layer dict of dw1 [4 H dh][d],
+    dw2 [d][H dh], drab [nb], all fp32 in the forward's weight layouts)."""
+    s = stream_handle(stream)
+    grads = [None] * model.num_layers
+    cur = dy
+    for li in reversed(range(stop_at, model.num_layers)):
+        sv = saved[li]
+        g = {"dw1": torch.empty(model.w1[li].shape, dtype=torch.float32, device=dy.device),
+             "dw2": torch.empty(model.w2[li].shape, dtype=torch.float32, device=dy.device),
+             "drab": torch.empty(model.rab[li].shape, dtype=torch.float32, device=dy.device)}
+        dx = torch.empty_like(cur)
+        a = hstu.hstu_layer_bwd_args()
+        a.dtype, a.d_model, a.eps, a.plan = model.dtype, model.d_model, model.eps, req.plan
+        a.x, a.w1t, a.w2t = sv["x"].data_ptr(), model.w1t[li].data_ptr(), model.w2t[li].data_ptr()
+        a.rab, a.num_buckets = model.rab[li].data_ptr(), model.rab[li].numel()
+        a.uvqk, a.s, a.o = sv["uvqk"].data_ptr(), sv["s"].data_ptr(), sv["o"].data_ptr()
+        a.dy, a.dx = cur.data_ptr(), dx.data_ptr()
+        a.dw1, a.dw2, a.drab = g["dw1"].data_ptr(), g["dw2"].data_ptr(), g["drab"].data_ptr()
+        need = hstu.hstu_layer_backward_workspace_size(a)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        hstu.hstu_layer_backward(a, s)
+        grads[li] = g
+        cur = dx
+    return cur, grads
 
 
 class Head:

@@ -311,6 +311,9 @@ typedef struct {
   void *uvqk_out;
   float *o_out;
   void *g_out;
+  /* optional device tap (bf16 only, NULL = skip): the pre-activation
+   * LayerNorm(x) . W1 [n_new_total][4*H*dh], which the backward needs */
+  void *s_out;
 } hstu_layer_args;
 
 hstu_status hstu_layer_workspace_size(const hstu_layer_args *args, size_t *bytes);
@@ -321,6 +324,50 @@ hstu_status hstu_layer_forward(const hstu_layer_args *args, hipStream_t stream);
  * layer i is x of layer i+1; all layers share the plan).  Stops at the first
  * failing layer and returns its status (the message names the layer). */
 hstu_status hstu_stack_forward(const hstu_layer_args *layers, int32_t n, hipStream_t stream);
+
+/* ======================================================================== */
+/* Backward of one layer, for training ["How Generative Recommenders Are    */
+/* Redefining RecSys at Scale", section HSTU support: training of HSTU]      */
+/* ======================================================================== */
+
+/* Gradients of a loss L with respect to the layer's input and parameters,
+ * given dL/dY, by the chain rule through the layer equations above.  Every
+ * position is computed (no cache): the plan is contiguous (page_size 0, every
+ * c_u = 0).  bf16 only; head_dim 128, H*head_dim <= 512.  The forward pass
+ * supplies what the backward reuses, through hstu_layer_forward's taps:
+ * uvqk_out (SiLU'd [U|V|Q|K]), s_out (the pre-activation) and o_out.
+ * Activation gradients are bf16, weight and bias gradients fp32.  drab is
+ * summed with LDS float atomics, so its low bits may differ between runs. */
+typedef struct {
+  hstu_dtype dtype;          /* HSTU_BF16 */
+  int32_t d_model;           /* multiple of 128, <= 2048 */
+  float eps;                 /* the forward's LayerNorm epsilon */
+  const hstu_plan *plan;     /* uploaded, contiguous */
+  const void *x;             /* device [n][d_model]: the layer's input */
+  /* W1 [d_model][4*H*dh] and W2 [H*dh][d_model] in the layout of x . W1 and
+   * g . W2 (the transposes of hstu_layer_args' w1 and w2), bf16 */
+  const void *w1t;
+  const void *w2t;
+  const float *rab;          /* device fp32 [num_buckets] (<= 256) */
+  int32_t num_buckets;
+  const void *uvqk;          /* forward taps: [n][4*H*dh] bf16 */
+  const void *s;             /*               [n][4*H*dh] bf16 */
+  const float *o;            /*               [n][H*dh] fp32 */
+  const void *dy;            /* device [n][d_model] bf16: dL/dY */
+  void *dx;                  /* device out [n][d_model] bf16 */
+  /* device out fp32, in hstu_layer_args' layouts: dw1 [4*H*dh][d_model],
+   * dw2 [d_model][H*dh]; drab [num_buckets] */
+  float *dw1;
+  float *dw2;
+  float *drab;
+  void *workspace;           /* device, >= hstu_layer_backward_workspace_size, 256-aligned */
+  size_t workspace_bytes;
+} hstu_layer_bwd_args;
+
+hstu_status hstu_layer_backward_workspace_size(const hstu_layer_bwd_args *args, size_t *bytes);
+/* Enqueues the backward on `stream`.  INVALID for bad arguments, UNSUPPORTED
+ * for a paged plan, cached positions, fp32 or unsupported sizes. */
+hstu_status hstu_layer_backward(const hstu_layer_bwd_args *args, hipStream_t stream);
 
 /* ======================================================================== */
 /* Multitask ranking head ["NVIDIA Dynamo-Triton Gets End-to-End HSTU       */
@@ -405,7 +452,8 @@ hstu_status hstu_batcher_pending(const hstu_batcher *batcher, int32_t *n);
 /* When enabled (non-zero), every kernel the library launches is bracketed
  * by a pair of HIP events recorded on the stream it is launched on.  Kernel
  * names: "layer_norm", "f1_gemm", "append", "attention", "reduce_gate",
- * "f2_gemm", "gather", "head".  Enabling or disabling clears the records. */
+ * "f2_gemm", "gather", "head", "bwd_attention", "bwd_gemm" (the backward's
+ * products), "bwd_rows" (its row and elementwise kernels).  Enabling or disabling clears the records. */
 hstu_status hstu_timing_enable(int32_t enable);
 /* Waits for the recorded events of `kernel` and returns the number of
  * launches and their summed duration in milliseconds; clears them.
