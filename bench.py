@@ -65,6 +65,7 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serving", action="store_true", help="skip the serving-loop latency measurement")
+    ap.add_argument("--no-training", action="store_true", help="skip the training-step measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (reference for HBM traffic counters)")
     args = ap.parse_args(argv)
@@ -183,6 +184,9 @@ def main(argv=None):
     serving_out = None
     if not args.no_serving and args.workload == "C4":
         serving_out = serving_results(w, args.seed)
+    training_out = None
+    if not args.no_training and args.workload == "C4":
+        training_out = training_results(args.seed)
     tier = host_tier_rates(scn) if scn.cache is not None else None   # attaches a host tier: last
 
     cpu = None
@@ -218,6 +222,7 @@ def main(argv=None):
         "candidate_tokens_per_s": round(sum(n_targets) / (ms_per_step / 1000.0), 1),
         "host_tier": tier,
         "serving": serving_out,
+        "training": training_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -263,6 +268,68 @@ def host_tier_rates(scn, reps=3):
         out[f"{kind}_ms"] = round(ms, 3)
         out[f"{kind}_GBps"] = round(moved / (ms * 1e-3) / 1e9, 2)
     return out
+
+
+def training_results(seed, steps=5, warmup=2):
+    """One training step of C2's model and batch (3 bf16 layers, batch 8,
+    histories uniform [1024, 4096] + 64 candidates, every position computed):
+    the forward keeping its taps, then hstu_layer_backward through every
+    layer for a seeded dL/dY.  Outside the timed request; inputs resident.
+    The backward attention's roofline uses 5 products per visible pair and
+    head (S recomputed, dP, dV, dK, dQ: 10 dh FLOPs per pair)."""
+    import torch
+
+    from generative_recommender_sequence_amd import hstu, runtime
+    from generative_recommender_sequence_amd.workloads import round_bf16, workload_for
+
+    w = workload_for("C2", seed)
+    cfg = w.cfg
+    scn = runtime.Scenario(w)
+    req, x = scn.make_request()
+    rng = np.random.default_rng([seed, 0xB3D])
+    n = int(sum(req.new_len))
+    dy = torch.from_numpy(round_bf16(rng.standard_normal((n, cfg.d_model)).astype(np.float32))).cuda().to(
+        torch.bfloat16)
+    ws = [None]
+
+    def step():
+        y, saved = runtime.forward_for_backward(scn.model, req, x)
+        dx, grads = runtime.backward(scn.model, req, saved, dy)
+        return dx
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / steps
+    hstu.hstu_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in hstu.TIMED_KERNELS:
+        cnt, tot = hstu.hstu_timing_read(name)
+        if cnt:
+            kern[name] = {"launches": cnt, "ms_per_step": round(tot / steps, 4)}
+    hstu.hstu_timing_enable(False)
+    pairs = float(req.info.pairs)
+    bwd_att_ms = kern["bwd_attention"]["ms_per_step"] / cfg.num_layers
+    flops = 10.0 * cfg.head_dim * cfg.num_heads * pairs
+    achieved = flops / (bwd_att_ms * 1e-3) / 1e12
+    req.close()
+    return {"workload": "C2 model and batch: 3 bf16 layers, batch 8, histories uniform [1024, 4096] + 64 "
+                        "candidates, forward (with taps) + backward, seeded dL/dY",
+            "tokens_per_step": n, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(n / (ms / 1000.0), 1),
+            "kernels_ms_per_step": {k: v["ms_per_step"] for k, v in kern.items()},
+            "backward_attention_roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                                            "algorithmic_flops_per_layer": flops,
+                                            "ms_per_layer": round(bwd_att_ms, 4)}}
 
 
 def serving_results(w, seed, users=32):

@@ -268,6 +268,7 @@ struct BwdLaunch {
   int32_t n_kv_items;
   const BwdQItem* q_items;
   int32_t n_q_items;
+  int32_t max_len;        // longest user (sizes the per-distance sums)
 };
 hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s);
 hipError_t launch_drab_sum(const float* part, int32_t items, int32_t nb, float* drab, hipStream_t s);

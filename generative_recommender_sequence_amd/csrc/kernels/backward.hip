@@ -22,6 +22,8 @@
 // of its key), which makes the score registers the A operand of dV += P^T dO
 // and dK += dZ^T Q directly; dO and Q are read transposed from LDS.  The
 // query-block kernel is laid out like the forward (rows are keys).
+#include <algorithm>
+
 #include "common.h"
 
 namespace hstu {
@@ -45,16 +47,18 @@ __device__ __forceinline__ v4i16 lds_read_tr(const lds_u16* p) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // MFMA row i of a 32-row block reads row perm(i): bits 2 and 3 swapped
 __device__ __forceinline__ int perm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
-// 16-byte-chunk XOR swizzles of [rows][128] bf16 tiles: rswz suits 16-lane
-// row reads, tswz suits the transposed reads
-__device__ __forceinline__ int rswz(int row) { return row & 15; }
-__device__ __forceinline__ int tswz(int row) { return (row & 3) << 2; }
+// 16-byte-chunk XOR swizzle of [rows][128] bf16 tiles, free of bank
+// conflicts for both kinds of operand read: 16 lanes reading one chunk of 16
+// consecutive rows see 16 distinct slots (the map is a bijection on row & 15),
+// and the transposed reads (4 consecutive rows x 2 adjacent chunks per 16
+// lanes) see 8 distinct slots (slot >> 1 differs across the 4 rows).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 __device__ __forceinline__ bf16x8 lds_row8(const lds_u16* p) {
   return *(const __attribute__((address_space(3))) bf16x8*)(p);
 }
 // B-type operand (8 consecutive rows of one column) of a [rows][128] tile
-// stored with tswz: column block nt (32 columns), rows 16 ks ..
+// stored with swz: column block nt (32 columns), rows 16 ks ..
 struct TrAddr {
   int a[2][4];
   __device__ __forceinline__ void init(int lane) {
@@ -66,7 +70,7 @@ struct TrAddr {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int d = 32 * nt + dcol;
-        a[r][nt] = row * DH + 8 * ((d >> 3) ^ tswz(row)) + (d & 7);
+        a[r][nt] = row * DH + 8 * ((d >> 3) ^ swz(row)) + (d & 7);
       }
     }
   }
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const uint16_t* __restric
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * i + lrow;
       const int m = m0 + r;
-      const int ch = 8 * (lslot ^ tswz(r));
+      const int ch = 8 * (lslot ^ swz(r));
       const uint16_t* sa = m < m_end ? A + static_cast<int64_t>(m) * lda + i0 + ch : zeros + ch;
       const uint16_t* sb = m < m_end ? B + static_cast<int64_t>(m) * ldb + j0 + ch : zeros + ch;
       dma16(sa, Ad + (16 * wave + 4 * i) * WT);
@@ -338,9 +342,15 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ p
 // ---------------------------------------------------------------------------
 // attention, per 128-key block: dK, dV and the rab gradient
 // ---------------------------------------------------------------------------
-constexpr int KB = 128;  // keys per item (4 waves x 32)
-constexpr int QT = 32;   // queries per step
-constexpr int kTab = QT + KB;  // distances per step (159 used)
+// Each wave owns 32 keys; a step covers 64 queries as two 32-query halves
+// whose products are issued together, so one half's SiLU work overlaps the
+// other half's MFMAs.  The rab gradient is summed per distance i - j in LDS
+// (an atomic add per visible pair, at most two lanes on one address; a wave
+// whose 32 x 32 pairs all fall in one bucket adds one wave sum), then folded
+// into buckets, and written as this item's partial.
+constexpr int KB = 128;        // keys per item (4 waves x 32)
+constexpr int QT = 64;         // queries per step
+constexpr int kTab = QT + KB;  // distances per step (191 used)
 
 __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   __shared__ __attribute__((aligned(16))) uint16_t Q0s[QT * DH];
@@ -348,9 +358,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   __shared__ __attribute__((aligned(16))) uint16_t Q1s[QT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t D1s[QT * DH];
   __shared__ float bias0[kTab], bias1[kTab];
-  __shared__ int bkt0[kTab], bkt1[kTab];
-  __shared__ float rab_s[256];
   __shared__ float drab_s[256];
+  extern __shared__ float dist_s[];  // [max_len + 64]: sum of dz per distance, then a spare slot per lane
   lds_u16* const Q0 = (lds_u16*)Q0s;
   lds_u16* const D0 = (lds_u16*)D0s;
   lds_u16* const Q1 = (lds_u16*)Q1s;
@@ -368,10 +377,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   const int wave = uniform(tid >> 6);
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
-  for (int i = tid; i < nb; i += 256) {
-    rab_s[i] = b.rab[i];
-    drab_s[i] = 0.f;
-  }
+  const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur; then 64 spare slots
+  for (int i = tid; i < nb; i += 256) drab_s[i] = 0.f;
+  for (int i = tid; i < ndist + 64; i += 256) dist_s[i] = 0.f;
   // this wave's keys as B operands (K for S = Q K^T, V for dP = dO V^T)
   bf16x8 kf[DH / 16], vf[DH / 16];
   {
@@ -388,83 +396,140 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
 #pragma unroll
   for (int t = 0; t < DH / 32; ++t) dv_acc[t] = dk_acc[t] = f32x16{};
 
-  // query tiles that see some key of the block
+  // query steps that see some key of the block
   const int kb_end = min(k0 + KB, L);
-  auto tile_vis = [&](int q0) {
+  auto step_vis = [&](int q0) {
     const int qe = min(q0 + QT, L);
     if (k0 < qe && q0 < kb_end) return true;
     return k0 < hist && k0 < qe - 1;
   };
-  // copy: wave w fills rows 8 w .. 8 w + 7 of Q and dO, four rows per instruction
+  // copy: wave w fills rows 16 w .. 16 w + 15 of Q and dO, four rows per instruction
   const int lrow = lane >> 4, lslot = lane & 15;
   auto copy_tile = [&](int q0, lds_u16* Qd, lds_u16* Dd) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * wave + 4 * i + lrow;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + lrow;
       const int q = min(q0 + r, L - 1);
-      const int ch = 8 * (lslot ^ tswz(r));
-      dma16(b.a + (row0 + q) * ST + 2 * inner + h * DH + ch, Qd + (8 * wave + 4 * i) * DH);
-      dma16(b.dO + static_cast<int64_t>(row0 + q) * inner + h * DH + ch, Dd + (8 * wave + 4 * i) * DH);
+      const int ch = 8 * (lslot ^ swz(r));
+      dma16(b.a + (row0 + q) * ST + 2 * inner + h * DH + ch, Qd + (16 * wave + 4 * i) * DH);
+      dma16(b.dO + static_cast<int64_t>(row0 + q) * inner + h * DH + ch, Dd + (16 * wave + 4 * i) * DH);
     }
   };
   // distance table of a step: entry t is distance (q0 - k0 - (KB - 1)) + t
-  auto fill_tab = [&](int q0, float* bias, int* bkt) {
+  auto fill_tab = [&](int q0, float* bias) {
     if (tid < kTab) {
       const int d = q0 - k0 - (KB - 1) + tid;
-      const int bk = d < 0 ? 0 : rel_bucket(d, nb);
-      bias[tid] = d < 0 ? 0.f : b.rab[bk];
-      bkt[tid] = bk;
+      bias[tid] = d < 0 ? 0.f : b.rab[rel_bucket(d, nb)];
     }
   };
   TrAddr tr;
   tr.init(lane);
-  int qaddr[DH / 16];  // A operand of S: query row perm(l32), chunk (2s + g)
+  int qaddr[DH / 16];  // A operand of S: query row perm(l32) (+ 32 per half), chunk (2s + g)
   {
     const int row = perm(l32);
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) qaddr[s] = row * DH + 8 * ((2 * s + g) ^ tswz(row));
+    for (int s = 0; s < DH / 16; ++s) qaddr[s] = row * DH + 8 * ((2 * s + g) ^ swz(row));
   }
 
-  auto step = [&](int q0, const lds_u16* Qs, const lds_u16* Ds, const float* bias, const int* bkt) {
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qs + qaddr[s]), kf[s], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Ds + qaddr[s]), vf[s], pacc, 0, 0, 0);
-    }
-    // register r holds query q0 + 16 (r / 8) + 8 g + r % 8 against this lane's key
-    const int dmin = q0 - (kw0 + 31), dmax = q0 + QT - 1 - kw0;
-    const bool full = kw0 + 31 < q0 && kw0 + 31 < hist && q0 + QT <= L && kw0 + 31 < L;
+  // register r of half hf holds query q0 + 32 hf + 16 (r / 8) + 8 g + r % 8 against this lane's key.
+  // Wave-uniform cases, each a straight loop: every pair visible in one
+  // bucket (one wave sum) or in at most four (one wave sum per bucket, split
+  // at the bucket edges), every pair visible (per-distance adds), or masked
+  // (a masked pair adds 0 to its lane's spare slot, so masked lanes do not
+  // pile onto one address).
+  auto elementwise = [&](int q0, int hf, f32x16& sacc, f32x16& pacc, const float* bias) {
+    const int qh = q0 + 32 * hf;
+    const int dmin = qh - (kw0 + 31), dmax = qh + 31 - kw0;
+    const bool full = kw0 + 31 < qh && kw0 + 31 < hist && qh + 32 <= L && kw0 + 31 < L;
     const bool uni = full && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
-    float dsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ql = 16 * (r >> 3) + 8 * g + (r & 7);
-      const int i = q0 + ql;
-      const int t = ql + (KB - 1) - (key - k0);
-      const float z = sacc[r] + bias[t];
+    const int tb = 32 * hf + (KB - 1) - (key - k0);  // table entry of register 0
+    const int sb = qh - key;                          // distance of register 0
+    auto pair = [&](int r, float& p, float& dz) {
+      const float z = sacc[r] + bias[tb + 16 * (r >> 3) + 8 * g + (r & 7)];
       const float sg = sigmoid(z);
-      float p = z * sg * inv_n;
-      float dz = pacc[r] * inv_n * sg * (1.0f + z * (1.0f - sg));
-      if (!full && !(i < L && key < L && visible(i, key, hist))) {
-        p = 0.f;
-        dz = 0.f;
-      }
-      sacc[r] = p;
-      pacc[r] = dz;
-      if (uni) {
-        dsum += dz;
-      } else if (dz != 0.f) {
-        atomicAdd(&drab_s[bkt[t]], dz);
-      }
-    }
+      p = z * sg * inv_n;
+      dz = pacc[r] * inv_n * sg * (1.0f + z * (1.0f - sg));
+    };
+    // up to four buckets: t[k] is the first distance of bucket blo + 1 + k
+    const int blo = full ? rel_bucket(dmin, nb) : 0;
+    const int bhi = full ? rel_bucket(dmax, nb) : 0;
+    const bool few = full && bhi - blo <= 3;
     if (uni) {
-      dsum = wave_sum(dsum);
-      if (lane == 0) atomicAdd(&drab_s[rel_bucket(dmax, nb)], dsum);
-    }
-    // dV += P^T dO, dK += dZ^T Q (k = the step's 32 queries)
+      float dsum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < QT / 16; ++ks) {
+      for (int r = 0; r < 16; ++r) {
+        float p, dz;
+        pair(r, p, dz);
+        sacc[r] = p;
+        pacc[r] = dz;
+        dsum += dz;
+      }
+      dsum = wave_sum(dsum);
+      if (lane == 0) atomicAdd(&drab_s[bhi], dsum);
+    } else if (few) {
+      int t[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (blo + 1 + k > bhi) {
+          t[k] = 1 << 30;
+          continue;
+        }
+        int lo = dmin, hi = dmax;  // bucket(lo) < blo + 1 + k <= bucket(hi)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (rel_bucket(mid, nb) >= blo + 1 + k) hi = mid; else lo = mid;
+        }
+        t[k] = hi;
+      }
+      float s_all = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p, dz;
+        pair(r, p, dz);
+        sacc[r] = p;
+        pacc[r] = dz;
+        const int dd = sb + 16 * (r >> 3) + 8 * g + (r & 7);
+        s_all += dz;
+        s1 += dd >= t[0] ? dz : 0.f;
+        s2 += dd >= t[1] ? dz : 0.f;
+        s3 += dd >= t[2] ? dz : 0.f;
+      }
+      s_all = wave_sum(s_all);
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
+      s3 = wave_sum(s3);
+      if (lane == 0) {
+        atomicAdd(&drab_s[blo], s_all - s1);
+        if (blo + 1 <= bhi) atomicAdd(&drab_s[blo + 1], s1 - s2);
+        if (blo + 2 <= bhi) atomicAdd(&drab_s[blo + 2], s2 - s3);
+        if (blo + 3 <= bhi) atomicAdd(&drab_s[blo + 3], s3);
+      }
+    } else if (full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p, dz;
+        pair(r, p, dz);
+        sacc[r] = p;
+        pacc[r] = dz;
+        atomicAdd(&dist_s[sb + 16 * (r >> 3) + 8 * g + (r & 7)], dz);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p, dz;
+        pair(r, p, dz);
+        const int i = qh + 16 * (r >> 3) + 8 * g + (r & 7);
+        const bool vis = (i < L) & (key < L) & ((key == i) | ((key < i) & (key < hist)));
+        sacc[r] = vis ? p : 0.f;
+        pacc[r] = vis ? dz : 0.f;
+        atomicAdd(&dist_s[vis ? i - key : ndist + lane], vis ? dz : 0.f);
+      }
+    }
+  };
+  // dV += P^T dO, dK += dZ^T Q over the half's 32 queries
+  auto accumulate = [&](int hf, const f32x16& sacc, const f32x16& pacc, const lds_u16* Qs, const lds_u16* Ds) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pa, za;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -473,41 +538,76 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
       }
 #pragma unroll
       for (int nt = 0; nt < DH / 32; ++nt) {
-        dv_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr.read(Ds, nt, ks), dv_acc[nt], 0, 0, 0);
-        dk_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, tr.read(Qs, nt, ks), dk_acc[nt], 0, 0, 0);
+        dv_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr.read(Ds, nt, 2 * hf + ks), dv_acc[nt], 0, 0, 0);
+        dk_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, tr.read(Qs, nt, 2 * hf + ks), dk_acc[nt], 0, 0, 0);
       }
     }
   };
+  auto step = [&](int q0, const lds_u16* Qs, const lds_u16* Ds, const float* bias) {
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) sacc[hf] = pacc[hf] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qs + qaddr[s] + 32 * hf * DH), kf[s], sacc[hf], 0, 0, 0);
+        pacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Ds + qaddr[s] + 32 * hf * DH), vf[s], pacc[hf], 0, 0, 0);
+      }
+    elementwise(q0, 0, sacc[0], pacc[0], bias);
+    accumulate(0, sacc[0], pacc[0], Qs, Ds);
+    elementwise(q0, 1, sacc[1], pacc[1], bias);
+    accumulate(1, sacc[1], pacc[1], Qs, Ds);
+  };
 
   int q0 = (k0 / QT) * QT;
-  while (q0 < L && !tile_vis(q0)) q0 += QT;
+  while (q0 < L && !step_vis(q0)) q0 += QT;
   if (q0 < L) {
-    fill_tab(q0, bias0, bkt0);
+    fill_tab(q0, bias0);
     copy_tile(q0, Q0, D0);
   }
-  __syncthreads();
+  __syncthreads();  // tables zeroed, first step staged
   while (q0 < L) {
     int qn = q0 + QT;
-    while (qn < L && !tile_vis(qn)) qn += QT;
+    while (qn < L && !step_vis(qn)) qn += QT;
     if (qn < L) {
-      fill_tab(qn, bias1, bkt1);
+      fill_tab(qn, bias1);
       copy_tile(qn, Q1, D1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kw0 < L) step(q0, Q0, D0, bias0, bkt0);
+    if (kw0 < L) step(q0, Q0, D0, bias0);
     __syncthreads();
     if (qn >= L) break;
     q0 = qn;
     qn = q0 + QT;
-    while (qn < L && !tile_vis(qn)) qn += QT;
+    while (qn < L && !step_vis(qn)) qn += QT;
     if (qn < L) {
-      fill_tab(qn, bias0, bkt0);
+      fill_tab(qn, bias0);
       copy_tile(qn, Q0, D0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kw0 < L) step(q0, Q1, D1, bias1, bkt1);
+    if (kw0 < L) step(q0, Q1, D1, bias1);
     __syncthreads();
     q0 = qn;
+  }
+  __syncthreads();
+  // fold the per-distance sums into buckets: thread t takes a contiguous run
+  // of distances (buckets rise with distance) and adds each bucket's run once
+  {
+    const int per = (ndist + 255) / 256;
+    const int d0 = tid * per, d1 = min(ndist, d0 + per);
+    float run = 0.f;
+    int cur = -1;
+    for (int dd = d0; dd < d1; ++dd) {
+      const int bk = rel_bucket(dd, nb);
+      if (bk != cur) {
+        if (cur >= 0 && run != 0.f) atomicAdd(&drab_s[cur], run);
+        cur = bk;
+        run = 0.f;
+      }
+      run += dist_s[dd];
+    }
+    if (cur >= 0 && run != 0.f) atomicAdd(&drab_s[cur], run);
   }
   __syncthreads();
   for (int i = tid; i < nb; i += 256) b.drab_partial[static_cast<int64_t>(blockIdx.x) * nb + i] = drab_s[i];
@@ -584,8 +684,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdLaunch b) {
       const int r = 16 * wave + 4 * i + lrow;
       const int kk = min(k0 + r, L - 1);
       const uint16_t* src = b.a + (row0 + kk) * ST + h * DH;
-      dma16(src + 3 * inner + 8 * (lslot ^ tswz(r)), Kd + (16 * wave + 4 * i) * DH);
-      dma16(src + 1 * inner + 8 * (lslot ^ rswz(r)), Vd + (16 * wave + 4 * i) * DH);
+      dma16(src + 3 * inner + 8 * (lslot ^ swz(r)), Kd + (16 * wave + 4 * i) * DH);
+      dma16(src + 1 * inner + 8 * (lslot ^ swz(r)), Vd + (16 * wave + 4 * i) * DH);
     }
   };
   // reversed distance table: entry t is distance qa + 127 - k0 - t
@@ -602,8 +702,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdLaunch b) {
     const int row = perm(l32);
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
-      kaddr[s] = row * DH + 8 * ((2 * s + g) ^ tswz(row));
-      vaddr[s] = row * DH + 8 * ((2 * s + g) ^ rswz(row));
+      kaddr[s] = row * DH + 8 * ((2 * s + g) ^ swz(row));
+      vaddr[s] = row * DH + 8 * ((2 * s + g) ^ swz(row));
     }
   }
 
@@ -618,19 +718,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdLaunch b) {
         pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Vs + vaddr[s] + 32 * mt * DH), df[s], pacc[mt], 0, 0, 0);
       }
     }
-    // register r of block mt: key k0 + 32 mt + 16 (r / 8) + 8 g + r % 8, query qpos
+    // register r of block mt: key k0 + 32 mt + 16 (r / 8) + 8 g + r % 8, query qpos;
+    // no mask when every key of the step is visible to every query of the wave
     const float* brow = &bias[127 - qlocal + 8 * g];
+    const bool full = k0 + KT - 1 < qa + wq0 && k0 + KT - 1 < hist && k0 + KT <= L && wq0 + 32 <= qb.count;
+    if (full) {
 #pragma unroll
-    for (int mt = 0; mt < KT / 32; ++mt)
+      for (int mt = 0; mt < KT / 32; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
-        const int j = k0 + 8 * g + koff;
-        const float z = sacc[mt][r] + brow[koff];
-        const float sg = sigmoid(z);
-        const float dz = pacc[mt][r] * inv_n * sg * (1.0f + z * (1.0f - sg));
-        sacc[mt][r] = (j < L && qlocal < qb.count && visible(qpos, j, hist)) ? dz : 0.f;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
+          const float z = sacc[mt][r] + brow[koff];
+          const float sg = sigmoid(z);
+          sacc[mt][r] = pacc[mt][r] * inv_n * sg * (1.0f + z * (1.0f - sg));
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < KT / 32; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * mt + 16 * (r >> 3) + (r & 7);
+          const int j = k0 + 8 * g + koff;
+          const float z = sacc[mt][r] + brow[koff];
+          const float sg = sigmoid(z);
+          const float dz = pacc[mt][r] * inv_n * sg * (1.0f + z * (1.0f - sg));
+          const bool vis = (j < L) & (qlocal < qb.count) & ((j == qpos) | ((j < qpos) & (j < hist)));
+          sacc[mt][r] = vis ? dz : 0.f;
+        }
+    }
     // dQ += dZ K (k = the step's keys; K read transposed)
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
@@ -747,8 +862,11 @@ hipError_t launch_wgrad(const void* A, int64_t lda, const void* B, int64_t ldb, 
 }
 
 hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
+  // per-distance rab-gradient sums of the longest user in LDS
+  const size_t dist_bytes = static_cast<size_t>(b.max_len + 64) * sizeof(float);
+  if (dist_bytes > (16384 + 64) * sizeof(float)) return hipErrorInvalidValue;
   if (b.n_kv_items > 0)
-    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(b.n_kv_items)), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(b.n_kv_items)), dim3(256), dist_bytes, s, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (b.n_q_items > 0)
@@ -756,20 +874,27 @@ hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-// drab[k] = sum over items of partial[item][k], in item order
+// drab[k] = sum over items of partial[item][k]: one block per bucket, thread
+// t sums items t, t + 256, ... in order, then a fixed-order tree
 namespace {
 __global__ __launch_bounds__(256) void drab_sum_kernel(const float* __restrict__ part, int32_t items, int32_t nb,
                                                        float* __restrict__ drab) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= nb) return;
+  __shared__ float red[256];
+  const int k = blockIdx.x, t = threadIdx.x;
   float s = 0.f;
-  for (int i = 0; i < items; ++i) s += part[static_cast<int64_t>(i) * nb + k];
-  drab[k] = s;
+  for (int i = t; i < items; i += 256) s += part[static_cast<int64_t>(i) * nb + k];
+  red[t] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) drab[k] = red[0];
 }
 }  // namespace
 
 hipError_t launch_drab_sum(const float* part, int32_t items, int32_t nb, float* drab, hipStream_t s) {
-  hipLaunchKernelGGL(drab_sum_kernel, dim3((nb + 255) / 256), dim3(256), 0, s, part, items, nb, drab);
+  hipLaunchKernelGGL(drab_sum_kernel, dim3(nb), dim3(256), 0, s, part, items, nb, drab);
   return hipGetLastError();
 }
 
