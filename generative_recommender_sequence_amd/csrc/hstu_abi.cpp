@@ -91,7 +91,12 @@ hstu_status fill_slot(StagingRing& r, const void* src, size_t bytes, StagingRing
   r.next = (r.next + 1) % 4;
   hstu_status st;
   if (sl.pending) {
-    if ((st = check_hip(hipEventSynchronize(sl.done), "staging")) != HSTU_OK) return st;
+    // poll rather than block: a blocking wait can sleep past the event, and
+    // the slot's previous upload is normally long done
+    hipError_t q;
+    while ((q = hipEventQuery(sl.done)) == hipErrorNotReady) {
+    }
+    if ((st = check_hip(q, "staging")) != HSTU_OK) return st;
     sl.pending = false;
   }
   if (!sl.done && (st = check_hip(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming), "staging")) != HSTU_OK)

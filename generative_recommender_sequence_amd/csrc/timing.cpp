@@ -77,6 +77,12 @@ hstu_status hstu_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(st.mu);
   st.clear();
   st.enabled = enable != 0;
+  // events made up front, so that recording them costs no creation on the launch path
+  while (st.enabled && st.spare.size() < 4096) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) break;
+    st.spare.push_back(e);
+  }
   return ok();
 }
 

@@ -145,7 +145,8 @@ class RequestBuffers:
         k = self.slot
         self.slot = (self.slot + 1) % len(self.pinned)
         if self.events[k] is not None:
-            self.events[k].synchronize()
+            while not self.events[k].query():  # poll: a blocking wait can oversleep
+                pass
         self.pinned[k][:n].numpy()[:] = pt.reshape(-1)
         dst = self.d_pt[:n]
         dst.copy_(self.pinned[k][:n], non_blocking=True)
