@@ -46,7 +46,7 @@ size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
 // Attention work per key tile is roughly constant, so pieces are sized in
 // visible tiles.  Enough pieces to give every CU several, but never pieces so
 // small that their partial tile costs more than the keys they read.
-constexpr int kTargetPieces = 1024;
+constexpr int kTargetPieces = 768;
 constexpr int kMinPieceTiles = 4;
 constexpr int kMaxPieceTiles = 256;  // bounds a work item's staged page-table slice
 constexpr int kXcds = 8;             // workgroups are dealt to the 8 XCDs round-robin
