@@ -49,31 +49,68 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void layer_norm_kernel(
 }
 
 // Each lane owns float4 chunks c = 4 * (lane + 64 k) of the row's H*dh values.
-template <typename T>
+// A block holds 4 rows of one q-block (blockIdx = q-block * 32 + row group),
+// so the q-block and user records are block-uniform loads, the slot ranges
+// depend only on the block and the lane's head, and the partial tiles are
+// fetched four slots at a time (summed in slot order, i.e. key order).
+constexpr int kGroups = kBlockQ / kRowsPerBlock;
+// four consecutive values of a row as float (8- or 16-byte accesses)
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{bf2f(r[0] & 0xFFFFu), bf2f(r[0] >> 16), bf2f(r[1] & 0xFFFFu), bf2f(r[1] >> 16)};
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16),
+                                       uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+template <typename T, int kChunks>  // inner <= 64 * 4 * kChunks
 __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
     PlanDev plan, const float* __restrict__ partials, float o_scale, const T* __restrict__ u,
     int64_t u_stride, float eps, float* __restrict__ o_out, T* __restrict__ g_out) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= plan.n_new) return;
+  const int qb = blockIdx.x / kGroups;
+  const int local = (blockIdx.x % kGroups) * kRowsPerBlock + (threadIdx.x >> 6);
   const int dh = plan.dh, H = plan.H, inner = H * dh;
-  const int qb = plan.row_qblock[row];
+  // slot ranges first: they need only the block and the lane's heads
+  SlotRange sr[kChunks];
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int c = 4 * (lane + 64 * k);
+    sr[k] = c < inner ? plan.qb_slots[qb * H + c / dh] : SlotRange{0, 0};
+  }
   const QBlock blk = plan.qblocks[qb];
-  const int local = row - blk.row0;
+  if (local >= blk.count) return;
+  const int row = blk.row0 + local;
   const float inv_n = plan.users[blk.user].inv_n * o_scale;
-  constexpr int kChunks = kMaxPerLane / 4;  // inner <= 64 * 32
+  // the gate's U, fetched while the partial tiles are summed
+  f32x4 uv[kChunks];
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int c = 4 * (lane + 64 * k);
+    uv[k] = (g_out && c < inner) ? load4(u + static_cast<int64_t>(row) * u_stride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   f32x4 o[kChunks];
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
-    int c = 4 * (lane + 64 * k);
+    const int c = 4 * (lane + 64 * k);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (c < inner) {
-      int h = c / dh, e = c % dh;
-      SlotRange sr = plan.qb_slots[qb * H + h];
-      for (int s = 0; s < sr.count; ++s) {
-        const float* p =
-            partials + (static_cast<int64_t>(sr.first + s) * kBlockQ + local) * dh + e;
-        acc += *reinterpret_cast<const f32x4*>(p);
+      const int e = c % dh;
+      const float* p = partials + (static_cast<int64_t>(sr[k].first) * kBlockQ + local) * dh + e;
+      const int64_t step = static_cast<int64_t>(kBlockQ) * dh;
+      for (int s = 0; s < sr[k].count; s += 4) {
+        const int left = sr[k].count - s;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(p + s * step);
+        const f32x4 v1 = left > 1 ? *reinterpret_cast<const f32x4*>(p + (s + 1) * step) : z;
+        const f32x4 v2 = left > 2 ? *reinterpret_cast<const f32x4*>(p + (s + 2) * step) : z;
+        const f32x4 v3 = left > 3 ? *reinterpret_cast<const f32x4*>(p + (s + 3) * step) : z;
+        acc += v0;
+        if (left > 1) acc += v1;
+        if (left > 2) acc += v2;
+        if (left > 3) acc += v3;
       }
       acc *= inv_n;
     }
@@ -104,16 +141,11 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) / inner + eps);
-  const T* ur = u + static_cast<int64_t>(row) * u_stride;
   T* gr = g_out + static_cast<int64_t>(row) * inner;
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
     int c = 4 * (lane + 64 * k);
-    if (c < inner) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        Elem<T>::store(gr + c + j, (o[k][j] - mean) * rstd * Elem<T>::load(ur + c + j));
-    }
+    if (c < inner) store4(gr + c, (o[k] - mean) * rstd * uv[k]);
   }
 }
 
@@ -138,15 +170,28 @@ hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* parti
                               float* o_out, void* g_out, hipStream_t s) {
   if (plan.n_new == 0) return hipSuccess;
   if (plan.H * plan.dh > 64 * kMaxPerLane) return hipErrorInvalidValue;
-  dim3 grid((plan.n_new + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
-  if (dtype == HSTU_BF16)
-    hipLaunchKernelGGL(reduce_gate_kernel<uint16_t>, grid, block, 0, s, plan, partials, o_scale,
-                       static_cast<const uint16_t*>(u), u_stride, eps, o_out,
-                       static_cast<uint16_t*>(g_out));
-  else
-    hipLaunchKernelGGL(reduce_gate_kernel<float>, grid, block, 0, s, plan, partials, o_scale,
-                       static_cast<const float*>(u), u_stride, eps, o_out,
-                       static_cast<float*>(g_out));
+  if (plan.n_qblocks == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(plan.n_qblocks) * kGroups), block(64 * kRowsPerBlock);
+  const bool narrow = plan.H * plan.dh <= 64 * 4 * 2;  // the configurations' 512 values a row
+  if (dtype == HSTU_BF16) {
+    auto* uu = static_cast<const uint16_t*>(u);
+    auto* gg = static_cast<uint16_t*>(g_out);
+    if (narrow)
+      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, 2>), grid, block, 0, s, plan, partials, o_scale, uu, u_stride,
+                         eps, o_out, gg);
+    else
+      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, kMaxPerLane / 4>), grid, block, 0, s, plan, partials, o_scale,
+                         uu, u_stride, eps, o_out, gg);
+  } else {
+    auto* uu = static_cast<const float*>(u);
+    auto* gg = static_cast<float*>(g_out);
+    if (narrow)
+      hipLaunchKernelGGL((reduce_gate_kernel<float, 2>), grid, block, 0, s, plan, partials, o_scale, uu, u_stride,
+                         eps, o_out, gg);
+    else
+      hipLaunchKernelGGL((reduce_gate_kernel<float, kMaxPerLane / 4>), grid, block, 0, s, plan, partials, o_scale, uu,
+                         u_stride, eps, o_out, gg);
+  }
   return hipGetLastError();
 }
 
