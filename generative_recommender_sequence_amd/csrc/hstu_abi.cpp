@@ -636,21 +636,24 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
     f.s_out = a->s_out;
     f.dh = dh;
     RowPages pg{};
+    pg.qblocks = p->dev.qblocks;
+    pg.n_qblocks = p->dev.n_qblocks;
     if (paged) {
       f.k_pool = c->k_pool;
       f.v_pool = c->v_pool;
       f.pool_layer_offset = L.pool_layer_offset;
       f.page_size = c->page_size;
       pg.page_table = a->d_page_table;
-      pg.row_qblock = p->dev.row_qblock;
-      pg.qblocks = p->dev.qblocks;
       pg.max_pages = p->desc.max_pages;
       pg.num_pages = c->num_pages;
       pg.H = H;
       pg.dh = dh;
       pg.page_size = c->page_size;
     }
-    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, info, M, d, a->eps, a->w1, colsum, 4 * inner, pg, stream); }),
+    // W1's column sums: the caller's precomputed ones, or this launch computes them
+    const int32_t cs_rows = a->w1_colsum ? 0 : 4 * inner;
+    if (a->w1_colsum) colsum = const_cast<float*>(a->w1_colsum);
+    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, info, M, d, a->eps, a->w1, colsum, cs_rows, pg, stream); }),
                         "hstu_layer_forward: row statistics")) != HSTU_OK)
       return st;
     if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, info, colsum, a->w1, f, M, 4 * inner, d, stream); }),
@@ -688,6 +691,14 @@ hstu_status hstu_stack_forward(const hstu_layer_args* layers, int32_t n, hipStre
     if (st != HSTU_OK) return fail(st, "hstu_stack_forward: layer " + std::to_string(i) + ": " + g_last_error);
   }
   return ok();
+}
+
+hstu_status hstu_w1_colsum(const void* w1, int32_t rows, int32_t d_model, float* out, hipStream_t stream) {
+  if (!w1 || !out || rows <= 0 || d_model <= 0 || d_model % 8 || d_model > 2048)
+    return fail(HSTU_ERR_INVALID, "hstu_w1_colsum: bad arguments");
+  RowPages pg{};  // no rows: only the column-sum blocks run
+  return check_hip(launch_row_stats(nullptr, nullptr, 0, d_model, 0.f, w1, out, rows, pg, stream),
+                   "hstu_w1_colsum");
 }
 
 // ---------------------------------------------------------------------------

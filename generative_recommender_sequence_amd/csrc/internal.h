@@ -202,12 +202,12 @@ struct RowInfo {
   float mean, rstd;
   int64_t pool_row;
 };
-// Paging of the new tokens (page_table == nullptr: none); rows are mapped to
-// (user, position) through the plan's q-blocks.
+// The rows by q-block (which map them to (user, position)) and the paging of
+// the new tokens (page_table == nullptr: none).
 struct RowPages {
   const int32_t* page_table;   // [B][max_pages]
-  const int32_t* row_qblock;   // [n_new]
-  const QBlock* qblocks;
+  const QBlock* qblocks;       // [n_qblocks], covering every new-token row
+  int32_t n_qblocks;
   int32_t max_pages, num_pages, H, dh, page_size;
 };
 // RowInfo of each row of a bf16 [rows][cols] matrix, and in the same launch

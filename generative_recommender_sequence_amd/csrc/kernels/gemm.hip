@@ -296,82 +296,114 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   }
 }
 
-// Per-row (mean, rstd) of x: one wave per row, two-pass from registers.
-// Blocks past the rows' blocks sum the rows of Wt (the column sums of W1 that
-// the f1 epilogue needs), one wave per row.
-constexpr int kStatRows = 4;
-__global__ __launch_bounds__(64 * kStatRows) void row_stats_kernel(const uint16_t* __restrict__ x,
-                                                                   RowInfo* __restrict__ info,
-                                                                   int32_t rows, int32_t cols,
-                                                                   float eps,
-                                                                   const uint16_t* __restrict__ wt,
-                                                                   float* __restrict__ colsum,
-                                                                   int32_t wt_rows, RowPages pg) {
+// Per-row (mean, rstd) of x, two-pass from registers.  A wave takes
+// kRowsPerWave rows (their loads issued together) of one q-block, a block
+// kStatWaves waves (blockIdx = q-block * kStatGroups + row group), so the
+// q-block record is a block-uniform load and each row's page slot one
+// dependent load.  Blocks past the rows' blocks sum the rows of Wt (the column
+// sums of W1 that the f1 epilogue needs) unless the caller supplies them.
+// One row a wave measured best: more rows a wave leave too few waves for the
+// small batches.
+constexpr int kStatWaves = 4;
+constexpr int kRowsPerWave = 1;
+constexpr int kStatGroups = kBlockQ / (kStatWaves * kRowsPerWave);
+template <int kMaxChunks>  // cols <= 64 * 8 * kMaxChunks
+__global__ __launch_bounds__(64 * kStatWaves) void row_stats_kernel(const uint16_t* __restrict__ x,
+                                                                    RowInfo* __restrict__ info,
+                                                                    int32_t rows, int32_t cols,
+                                                                    float eps,
+                                                                    const uint16_t* __restrict__ wt,
+                                                                    float* __restrict__ colsum,
+                                                                    int32_t wt_rows, RowPages pg) {
   const int lane = threadIdx.x & 63;
-  const int stat_blocks = (rows + kStatRows - 1) / kStatRows;
-  constexpr int kMaxChunks = 4;  // cols <= 64 * 8 * 4
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stat_blocks = pg.n_qblocks * kStatGroups;
+  auto unpack = [](u32x4 raw, float* f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      f[e] = bf2f(static_cast<uint16_t>((e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu)));
+  };
   if (static_cast<int>(blockIdx.x) >= stat_blocks) {
-    const int n = (blockIdx.x - stat_blocks) * kStatRows + (threadIdx.x >> 6);
-    if (n >= wt_rows) return;
-    const uint16_t* wr = wt + static_cast<int64_t>(n) * cols;
-    float s = 0.f;
+    const int n0 = ((blockIdx.x - stat_blocks) * kStatWaves + wave) * kRowsPerWave;
+    u32x4 raw[kRowsPerWave][kMaxChunks];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        const int col = 8 * (lane + 64 * c);
+        raw[r][c] = (n0 + r < wt_rows && col < cols)
+                        ? *reinterpret_cast<const u32x4*>(wt + static_cast<int64_t>(n0 + r) * cols + col)
+                        : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        float f[8];
+        unpack(raw[r][c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += f[e];
+      }
+      s = wave_sum(s);
+      if (lane == 0 && n0 + r < wt_rows) colsum[n0 + r] = s;
+    }
+    return;
+  }
+  const QBlock qb = pg.qblocks[blockIdx.x / kStatGroups];
+  const int l0 = ((blockIdx.x % kStatGroups) * kStatWaves + wave) * kRowsPerWave;
+  if (l0 >= qb.count) return;
+  u32x4 raw[kRowsPerWave][kMaxChunks];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
       const int col = 8 * (lane + 64 * c);
-      if (col < cols) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(wr + col);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s += bf2f(static_cast<uint16_t>((e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu)));
-      }
+      raw[r][c] = (l0 + r < qb.count && col < cols)
+                      ? *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(qb.row0 + l0 + r) * cols + col)
+                      : u32x4{0u, 0u, 0u, 0u};
     }
-    s = wave_sum(s);
-    if (lane == 0) colsum[n] = s;
-    return;
-  }
-  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kStatRows + (threadIdx.x >> 6));
-  if (row >= rows) return;
-  // the page slot this new token's K/V rows go to (-1: none); the row is
-  // wave-uniform, so these are scalar loads that overlap the row's loads
-  int64_t pool_row = -1;
-  if (pg.page_table) {
-    const QBlock qb = pg.qblocks[pg.row_qblock[row]];
-    const int pos = qb.pos0 + (row - qb.row0);
-    const int lp = pos / pg.page_size;
-    if (lp < pg.max_pages) {
-      const int page = pg.page_table[static_cast<int64_t>(qb.user) * pg.max_pages + lp];
-      if (page >= 0 && page < pg.num_pages)
-        pool_row = (static_cast<int64_t>(page) * pg.H * pg.page_size + (pos - lp * pg.page_size)) * pg.dh;
-    }
-  }
-  const uint16_t* xr = x + static_cast<int64_t>(row) * cols;
-  float v[kMaxChunks * 8];
-  float s = 0.f;
+  // the page slot each new token's K/V rows go to (-1: none)
+  int64_t pool_row[kRowsPerWave];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const int col = 8 * (lane + 64 * c);
-    u32x4 raw = col < cols ? *reinterpret_cast<const u32x4*>(xr + col) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float f = bf2f(static_cast<uint16_t>((e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu)));
-      v[8 * c + e] = f;
-      s += f;
-    }
-  }
-  const float mean = wave_sum(s) / cols;
-  float q = 0.f;
-#pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (8 * (lane + 64 * c) < cols) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float dv = v[8 * c + e] - mean;
-        q += dv * dv;
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    pool_row[r] = -1;
+    if (pg.page_table && l0 + r < qb.count) {
+      const int pos = qb.pos0 + l0 + r;
+      const int lp = pos / pg.page_size;
+      if (lp < pg.max_pages) {
+        const int page = pg.page_table[static_cast<int64_t>(qb.user) * pg.max_pages + lp];
+        if (page >= 0 && page < pg.num_pages)
+          pool_row[r] = (static_cast<int64_t>(page) * pg.H * pg.page_size + (pos - lp * pg.page_size)) * pg.dh;
       }
     }
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) / cols + eps);
-  if (lane == 0) info[row] = RowInfo{mean, rstd, pool_row};
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    if (l0 + r >= qb.count) break;
+    float v[kMaxChunks * 8];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      unpack(raw[r][c], &v[8 * c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[8 * c + e];
+    }
+    const float mean = wave_sum(s) / cols;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (8 * (lane + 64 * c) < cols) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dv = v[8 * c + e] - mean;
+          q += dv * dv;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / cols + eps);
+    if (lane == 0) info[qb.row0 + l0 + r] = RowInfo{mean, rstd, pool_row[r]};
+  }
 }
 
 constexpr int FT = 64, FK = 16;
@@ -434,12 +466,18 @@ __global__ __launch_bounds__(256) void head_finalize_kernel(const float* __restr
 hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
                             const void* w1t, float* colsum, int32_t w1t_rows, const RowPages& pg,
                             hipStream_t s) {
-  if (rows == 0) return hipSuccess;
+  if (rows == 0 && w1t_rows == 0) return hipSuccess;
   if (cols % 8 != 0 || cols > 64 * 8 * 4) return hipErrorInvalidValue;
-  const int blocks = (rows + kStatRows - 1) / kStatRows + (w1t_rows + kStatRows - 1) / kStatRows;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(blocks), dim3(64 * kStatRows), 0, s,
-                     static_cast<const uint16_t*>(x), info, rows, cols, eps,
-                     static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
+  const int per_block = kStatWaves * kRowsPerWave;
+  const int blocks = pg.n_qblocks * kStatGroups + (w1t_rows + per_block - 1) / per_block;
+  if (cols <= 64 * 8)
+    hipLaunchKernelGGL(row_stats_kernel<1>, dim3(blocks), dim3(64 * kStatWaves), 0, s,
+                       static_cast<const uint16_t*>(x), info, rows, cols, eps,
+                       static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
+  else
+    hipLaunchKernelGGL(row_stats_kernel<4>, dim3(blocks), dim3(64 * kStatWaves), 0, s,
+                       static_cast<const uint16_t*>(x), info, rows, cols, eps,
+                       static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
   return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ class hstu_layer_args(ctypes.Structure):
                 ("y", c_vp), ("w1", c_vp), ("w2", c_vp), ("rab", c_vp), ("num_buckets", c_i32),
                 ("cache", c_vp), ("layer", c_i32), ("d_page_table", c_vp), ("workspace", c_vp),
                 ("workspace_bytes", c_size), ("uvqk_out", c_vp), ("o_out", c_vp), ("g_out", c_vp),
-                ("s_out", c_vp)]
+                ("s_out", c_vp), ("w1_colsum", c_vp)]
 
 
 class hstu_layer_bwd_args(ctypes.Structure):
@@ -109,6 +109,7 @@ SIGNATURES = {
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
     "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
+    "hstu_w1_colsum": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "hstu_layer_backward_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_bwd_args), ctypes.POINTER(c_size)]),
     "hstu_layer_backward": (c_i32, [ctypes.POINTER(hstu_layer_bwd_args), c_vp]),
     "hstu_head_workspace_size": (c_i32, [ctypes.POINTER(hstu_head_args), ctypes.POINTER(c_size)]),
@@ -422,6 +423,10 @@ def hstu_stack_forward(layers, stream: int):
     else:
         arr = layers
     _check(lib().hstu_stack_forward(arr, len(arr), stream), "hstu_stack_forward")
+
+
+def hstu_w1_colsum(w1: int, rows: int, d_model: int, out: int, stream: int):
+    _check(lib().hstu_w1_colsum(w1, rows, d_model, out, stream or None), "hstu_w1_colsum")
 
 
 def hstu_layer_backward_workspace_size(args: hstu_layer_bwd_args) -> int:

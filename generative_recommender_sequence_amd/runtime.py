@@ -56,6 +56,13 @@ class Model:
         # W1 [d][4 H dh] and W2 [H dh][d] in the layout of x . W1 and g . W2 (the backward's operands)
         self.w1t = [w.t().contiguous() for w in self.w1]
         self.w2t = [w.t().contiguous() for w in self.w2]
+        # W1's column sums, computed once for the bf16 layer's fused pre-norm
+        self.w1_colsum = [None] * len(self.w1)
+        if dtype == HSTU_BF16 and str(device).startswith("cuda"):
+            for li, w in enumerate(self.w1):
+                cs = torch.empty(w.shape[0], dtype=torch.float32, device=device)
+                hstu.hstu_w1_colsum(w.data_ptr(), w.shape[0], w.shape[1], cs.data_ptr(), stream_handle())
+                self.w1_colsum[li] = cs
 
     @property
     def num_layers(self) -> int:
@@ -233,6 +240,8 @@ def layer_args(model: Model, req: Request, li: int, x: torch.Tensor, y: torch.Te
     a.w2 = model.w2[li].data_ptr()
     a.rab = model.rab[li].data_ptr()
     a.num_buckets = model.rab[li].numel()
+    if model.w1_colsum[li] is not None:
+        a.w1_colsum = model.w1_colsum[li].data_ptr()
     if cache is not None:
         a.cache = cache.h
         a.layer = li

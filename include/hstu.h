@@ -314,7 +314,16 @@ typedef struct {
   /* optional device tap (bf16 only, NULL = skip): the pre-activation
    * LayerNorm(x) . W1 [n_new_total][4*H*dh], which the backward needs */
   void *s_out;
+  /* optional (bf16): W1's column sums from hstu_w1_colsum for these weights
+   * (device fp32 [4*H*dh]); NULL: computed in every call */
+  const float *w1_colsum;
 } hstu_layer_args;
+
+/* The column sums of W1 that the bf16 layer's fused pre-norm uses (the sum
+ * over d_model of each output column), computed once per weight set: w1 as
+ * in hstu_layer_args (device bf16 [rows][d_model], rows = 4*H*dh), out device
+ * fp32 [rows].  The values equal those a call without them computes. */
+hstu_status hstu_w1_colsum(const void *w1, int32_t rows, int32_t d_model, float *out, hipStream_t stream);
 
 hstu_status hstu_layer_workspace_size(const hstu_layer_args *args, size_t *bytes);
 hstu_status hstu_layer_forward(const hstu_layer_args *args, hipStream_t stream);

@@ -112,3 +112,46 @@ def test_cached_prefix_plus_append_equals_full_recompute(dtype):
     assert err < (2 * TOL[full.dtype] if dtype == "bf16" else 1e-4)
     req_f.close()
     req_c.close()
+
+
+def test_layers_wide_model_bf16():
+    """d_model 1024 against H*dh 256 (wider rows than the configurations'):
+    the pre-norm statistics take four 512-value chunks a lane group."""
+    say("wide model bf16 d=1024")
+    cfg = small_config(dtype="bf16", d_model=1024, num_heads=2, head_dim=128, num_layers=2, n_targets=8,
+                       cache="hit", page_size=32)
+    hist = [90, 300]
+    w = generate(cfg, 4, batch=len(hist), hist_override=hist)
+    w.hit = np.ones(len(hist), bool)
+    w.prefill_order = np.arange(len(hist), dtype=np.int32)
+    w.num_pages = sum(-(-(h + 8) // 32) for h in hist) + 3
+    w.page_perm = np.random.default_rng(5).permutation(w.num_pages).astype(np.int32)
+    w.cfg = dataclasses.replace(cfg, batch=len(hist))
+    for lw in w.layers:
+        lw.w1 *= 4.0
+        lw.w2 *= 4.0
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    req, x = scn.make_request()
+    per = run_layers_with_taps(scn, req, x)
+    worst = check_layers(scn, req, per, [0, 1], "wide")
+    _assert_within(worst, TOL[scn.dtype])
+    req.close()
+
+
+def test_precomputed_w1_colsum_is_identical():
+    """The layer with W1's column sums from hstu_w1_colsum and with the sums
+    computed in the call give bit-identical outputs."""
+    say("precomputed W1 column sums")
+    w = _small("hit", "bf16", hist=[200, 33], T=16, layers=1)
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    req, x = scn.make_request()
+    y1 = runtime.forward(scn.model, req, x, scn.cache).clone()
+    saved = scn.model.w1_colsum
+    scn.model.w1_colsum = [None] * len(saved)
+    y2 = runtime.forward(scn.model, req, x, scn.cache).clone()   # appends the same K/V again
+    scn.model.w1_colsum = saved
+    torch.cuda.synchronize()
+    assert saved[0] is not None and torch.equal(y1, y2)
+    req.close()
