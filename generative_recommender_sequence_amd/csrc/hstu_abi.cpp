@@ -226,15 +226,12 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
   p->n_new = static_cast<int32_t>(q_row);
 
   // q-blocks
-  p->row_qblock.resize(p->n_new);
+  p->row_pos.resize(p->n_new);
   for (int32_t u = 0; u < B; ++u) {
     const UserInfo& ui = p->users[u];
-    for (int32_t r = 0; r < ui.n_new; r += kBlockQ) {
-      QBlock qb{u, ui.q_row0 + r, std::min(kBlockQ, ui.n_new - r), ui.start + r};
-      for (int32_t k = 0; k < qb.count; ++k)
-        p->row_qblock[qb.row0 + k] = static_cast<int32_t>(p->qblocks.size());
-      p->qblocks.push_back(qb);
-    }
+    for (int32_t r = 0; r < ui.n_new; ++r) p->row_pos[ui.q_row0 + r] = RowPos{u, ui.start + r};
+    for (int32_t r = 0; r < ui.n_new; r += kBlockQ)
+      p->qblocks.push_back(QBlock{u, ui.q_row0 + r, std::min(kBlockQ, ui.n_new - r), ui.start + r});
   }
   // visible key tiles of each q-block, then pieces
   const int32_t nqb = static_cast<int32_t>(p->qblocks.size());
@@ -337,7 +334,7 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
   p->off_qblocks = region(p->qblocks.size() * sizeof(QBlock));
   p->off_qb_slots = region(p->qb_slots.size() * sizeof(SlotRange));
   p->off_users = region(p->users.size() * sizeof(UserInfo));
-  p->off_row_qblock = region(p->row_qblock.size() * sizeof(int32_t));
+  p->off_row_pos = region(p->row_pos.size() * sizeof(RowPos));
   p->off_new_offsets = region(p->new_offsets.size() * sizeof(int32_t));
   p->off_start_pos = region(p->start_pos.size() * sizeof(int32_t));
   blob.assign(off, 0);
@@ -348,7 +345,7 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
   copy(p->off_qblocks, p->qblocks.data(), p->qblocks.size() * sizeof(QBlock));
   copy(p->off_qb_slots, p->qb_slots.data(), p->qb_slots.size() * sizeof(SlotRange));
   copy(p->off_users, p->users.data(), p->users.size() * sizeof(UserInfo));
-  copy(p->off_row_qblock, p->row_qblock.data(), p->row_qblock.size() * sizeof(int32_t));
+  copy(p->off_row_pos, p->row_pos.data(), p->row_pos.size() * sizeof(RowPos));
   copy(p->off_new_offsets, p->new_offsets.data(), p->new_offsets.size() * sizeof(int32_t));
   copy(p->off_start_pos, p->start_pos.data(), p->start_pos.size() * sizeof(int32_t));
   *out = p;
@@ -386,7 +383,7 @@ hstu_status hstu_plan_upload(hstu_plan* p, void* d_meta, size_t bytes, hipStream
   dv.qblocks = reinterpret_cast<const QBlock*>(base + p->off_qblocks);
   dv.qb_slots = reinterpret_cast<const SlotRange*>(base + p->off_qb_slots);
   dv.users = reinterpret_cast<const UserInfo*>(base + p->off_users);
-  dv.row_qblock = reinterpret_cast<const int32_t*>(base + p->off_row_qblock);
+  dv.row_pos = reinterpret_cast<const RowPos*>(base + p->off_row_pos);
   dv.new_offsets = reinterpret_cast<const int32_t*>(base + p->off_new_offsets);
   dv.start_pos = reinterpret_cast<const int32_t*>(base + p->off_start_pos);
   dv.n_items = static_cast<int32_t>(p->items.size());
@@ -531,7 +528,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
 
 namespace {
 struct LayerWs {
-  size_t xhat, colsum, uvqk, partials, g, total;
+  size_t xhat, colsum, slots, uvqk, partials, g, total;
 };
 // bf16 keeps only the row statistics of x (8 bytes a row) and the column sums
 // of W1 where fp32 keeps the normalised copy
@@ -540,9 +537,11 @@ LayerWs layer_ws(const hstu_plan* p, int dtype, int d_model) {
   LayerWs w{};
   size_t off = 0;
   w.xhat = off;
-  // bf16: row records [n] (statistics and page slot), then the f1 column sums [4 inner] fp32
-  w.colsum = align256(off + n * sizeof(RowInfo) + 1);
-  off = dtype == HSTU_BF16 ? align256(w.colsum + 4 * inner * sizeof(float) + 1)
+  // bf16: row statistics [n] (one slot a row), the f1 column sums [4 inner]
+  // fp32 and the rows' pool slots [n] int64
+  w.colsum = align256(off + n * sizeof(RowStat) + 1);
+  w.slots = align256(w.colsum + 4 * inner * sizeof(float) + 1);
+  off = dtype == HSTU_BF16 ? align256(w.slots + n * sizeof(int64_t) + 1)
                            : align256(off + n * d_model * esize(dtype) + 1);
   w.uvqk = off;
   off = align256(off + n * 4 * inner * esize(dtype) + 1);
@@ -574,6 +573,12 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   if (!(a->eps >= 0.f)) return fail(HSTU_ERR_INVALID, "hstu_layer_forward: eps must be >= 0");
   if (a->s_out && a->dtype != HSTU_BF16)
     return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_forward: the s_out tap is bf16 only");
+  if ((a->x_stats || a->y_stats) && (a->dtype != HSTU_BF16 || d > 128 * kMaxStatSlots))
+    return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_forward: x_stats / y_stats need bf16 and d_model <= 512");
+  if (a->row_slots && a->dtype != HSTU_BF16)
+    return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_forward: row_slots is bf16 only");
+  if (a->x_stats && p->desc.page_size > 0 && !a->row_slots)
+    return fail(HSTU_ERR_INVALID, "hstu_layer_forward: x_stats on a paged plan needs row_slots");
   if (p->n_new == 0) return ok();
   if (!a->x || !a->y || !a->w1 || !a->w2 || !a->rab || a->num_buckets <= 0)
     return fail(HSTU_ERR_INVALID, "hstu_layer_forward: null x/y/w1/w2/rab or no buckets");
@@ -625,9 +630,10 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   }
   const hstu_kv_cache* c = a->cache;
   if (a->dtype == HSTU_BF16) {
-    // row records (statistics, page slots) and W1's column sums, then f1 with
-    // the pre-norm, SiLU and the K/V append fused
-    auto* info = static_cast<RowInfo*>(xhat);
+    // row statistics (unless the previous layer's f2 left them) and W1's
+    // column sums (unless precomputed), then f1 with the pre-norm, SiLU and
+    // the K/V append fused
+    auto* row_stats = static_cast<RowStat*>(xhat);
     float* colsum = reinterpret_cast<float*>(ws + w.colsum);
     F1Args f{};
     f.uvqk = uvqk;
@@ -635,28 +641,38 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
     f.kv_to_uvqk = a->uvqk_out != nullptr;
     f.s_out = a->s_out;
     f.dh = dh;
-    RowPages pg{};
-    pg.qblocks = p->dev.qblocks;
-    pg.n_qblocks = p->dev.n_qblocks;
+    f.eps = a->eps;
+    // the rows' pool slots: looked up with the statistics, or the caller's
+    // from an earlier layer of the request
+    RowSlots sl{};
+    int64_t* row_slots = a->row_slots ? a->row_slots : reinterpret_cast<int64_t*>(ws + w.slots);
     if (paged) {
       f.k_pool = c->k_pool;
       f.v_pool = c->v_pool;
       f.pool_layer_offset = L.pool_layer_offset;
       f.page_size = c->page_size;
-      pg.page_table = a->d_page_table;
-      pg.max_pages = p->desc.max_pages;
-      pg.num_pages = c->num_pages;
-      pg.H = H;
-      pg.dh = dh;
-      pg.page_size = c->page_size;
+      f.row_slots = row_slots;
+      if (!a->x_stats) {
+        sl.out = row_slots;
+        sl.row_pos = p->dev.row_pos;
+        sl.page_table = a->d_page_table;
+        sl.max_pages = p->desc.max_pages;
+        sl.num_pages = c->num_pages;
+        sl.H = H;
+        sl.dh = dh;
+        sl.page_size = c->page_size;
+      }
     }
-    // W1's column sums: the caller's precomputed ones, or this launch computes them
+    const int32_t stat_rows = a->x_stats ? 0 : M;
     const int32_t cs_rows = a->w1_colsum ? 0 : 4 * inner;
+    const RowStat* x_stats = a->x_stats ? reinterpret_cast<const RowStat*>(a->x_stats) : row_stats;
+    const int32_t slots = a->x_stats ? d / 128 : 1;
     if (a->w1_colsum) colsum = const_cast<float*>(a->w1_colsum);
-    if ((st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, info, M, d, a->eps, a->w1, colsum, cs_rows, pg, stream); }),
+    if ((stat_rows || cs_rows) &&
+        (st = check_hip(timed(TK_LAYER_NORM, stream, [&] { return launch_row_stats(a->x, row_stats, stat_rows, d, a->w1, colsum, cs_rows, sl, stream); }),
                         "hstu_layer_forward: row statistics")) != HSTU_OK)
       return st;
-    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, info, colsum, a->w1, f, M, 4 * inner, d, stream); }),
+    if ((st = check_hip(timed(TK_F1, stream, [&] { return launch_f1_bf16(a->x, x_stats, slots, colsum, a->w1, f, M, 4 * inner, d, stream); }),
                         "hstu_layer_forward: f1")) != HSTU_OK)
       return st;
   } else {
@@ -680,7 +696,8 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
                                          a->o_out, g, stream); }),
                       "hstu_layer_forward: LayerNorm gate")) != HSTU_OK)
     return st;
-  return check_hip(timed(TK_F2, stream, [&] { return launch_gemm(a->dtype, 1, g, a->w2, a->y, a->x, M, d, inner, stream); }),
+  return check_hip(timed(TK_F2, stream, [&] { return launch_gemm(a->dtype, 1, g, a->w2, a->y, a->x, M, d, inner, stream,
+                                                                reinterpret_cast<RowStat*>(a->y_stats)); }),
                    "hstu_layer_forward: f2");
 }
 
@@ -696,8 +713,8 @@ hstu_status hstu_stack_forward(const hstu_layer_args* layers, int32_t n, hipStre
 hstu_status hstu_w1_colsum(const void* w1, int32_t rows, int32_t d_model, float* out, hipStream_t stream) {
   if (!w1 || !out || rows <= 0 || d_model <= 0 || d_model % 8 || d_model > 2048)
     return fail(HSTU_ERR_INVALID, "hstu_w1_colsum: bad arguments");
-  RowPages pg{};  // no rows: only the column-sum blocks run
-  return check_hip(launch_row_stats(nullptr, nullptr, 0, d_model, 0.f, w1, out, rows, pg, stream),
+  // no statistics rows: only the column-sum blocks run
+  return check_hip(launch_row_stats(nullptr, nullptr, 0, d_model, w1, out, rows, RowSlots{}, stream),
                    "hstu_w1_colsum");
 }
 

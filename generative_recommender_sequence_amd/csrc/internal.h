@@ -49,6 +49,11 @@ struct QBlock {
   int32_t user, row0, count, pos0;
 };
 
+// User and sequence position of a new-token row.
+struct RowPos {
+  int32_t user, pos;
+};
+
 // Per-user scalars the kernels read.
 struct UserInfo {
   int32_t q_row0;     // first new-token row
@@ -67,7 +72,7 @@ struct PlanDev {
   const QBlock* qblocks;
   const SlotRange* qb_slots;  // [n_qblocks][H]
   const UserInfo* users;
-  const int32_t* row_qblock;  // [n_new]: q-block of each new-token row
+  const RowPos* row_pos;      // [n_new]
   const int32_t* new_offsets; // [B+1]
   const int32_t* start_pos;   // [B]
   int32_t n_items, n_qblocks, n_new, B, H, dh, page_size, max_pages, max_len;
@@ -83,11 +88,12 @@ struct hstu_plan {
   std::vector<hstu::QBlock> qblocks;
   std::vector<hstu::SlotRange> qb_slots;
   std::vector<hstu::UserInfo> users;
-  std::vector<int32_t> row_qblock, new_offsets, start_pos;
+  std::vector<hstu::RowPos> row_pos;
+  std::vector<int32_t> new_offsets, start_pos;
   int32_t n_slots = 0, n_new = 0, max_len = 0;
   int64_t pairs = 0;
   std::vector<unsigned char> host_blob;  // packed image of the device metadata
-  size_t off_items = 0, off_qblocks = 0, off_qb_slots = 0, off_users = 0, off_row_qblock = 0,
+  size_t off_items = 0, off_qblocks = 0, off_qb_slots = 0, off_users = 0, off_row_pos = 0,
          off_new_offsets = 0, off_start_pos = 0;
   void* d_meta = nullptr;  // set by hstu_plan_upload
   hstu::PlanDev dev{};
@@ -190,45 +196,53 @@ inline float partial_scale(int dtype) { return dtype == HSTU_BF16 ? kBf16Partial
 hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows, int32_t cols,
                              float eps, hipStream_t s);
 
-// C[M][N] = epilogue(A[M][K] . Wt[N][K]^T); epilogue 0: SiLU, 1: + residual R[M][N]
-// (bf16: epilogue 1 only; f1 goes through launch_f1_bf16)
-hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
-                       const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s);
-
-// Per new-token row of the bf16 path: LayerNorm statistics of x and the
-// element offset, within one layer of the pools, of the row's (page, head 0,
-// slot) for the K/V append (-1: not appended).
-struct RowInfo {
-  float mean, rstd;
-  int64_t pool_row;
+// Statistics of a row of a bf16 activation, in slots: slot t holds the mean
+// and the sum of squared deviations from it of the t-th of the row's equal
+// column shares; the LayerNorm statistics combine them (the pairwise update
+// of Chan, Golub and LeVeque).  f2 writes one slot per 128-column tile of its
+// output (the next layer's input); the row-statistics kernel one slot per row.
+struct RowStat {
+  float mean, m2;
 };
-// The rows by q-block (which map them to (user, position)) and the paging of
-// the new tokens (page_table == nullptr: none).
-struct RowPages {
-  const int32_t* page_table;   // [B][max_pages]
-  const QBlock* qblocks;       // [n_qblocks], covering every new-token row
-  int32_t n_qblocks;
+constexpr int kMaxStatSlots = 4;
+
+// C[M][N] = epilogue(A[M][K] . Wt[N][K]^T); epilogue 0: SiLU, 1: + residual
+// R[M][N], 3 (bf16 only): plain.  bf16 takes epilogues 1 and 3 (f1 goes
+// through launch_f1_bf16); its epilogue 1 may also write the RowStat slots of
+// C's rows, one per 128-column tile, to y_stats (nullptr: not kept).
+hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
+                       const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s,
+                       RowStat* y_stats = nullptr);
+
+// Where each new-token row's K/V go in one layer of the pools.
+struct RowSlots {
+  int64_t* out;               // [rows]: element offset of (page, head 0, slot), or -1 (nullptr: not computed)
+  const RowPos* row_pos;      // [rows]
+  const int32_t* page_table;  // [B][max_pages]
   int32_t max_pages, num_pages, H, dh, page_size;
 };
-// RowInfo of each row of a bf16 [rows][cols] matrix, and in the same launch
-// the row sums of w1t (bf16 [w1t_rows][cols]) -> colsum
-hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
-                            const void* w1t, float* colsum, int32_t w1t_rows, const RowPages& pg,
-                            hipStream_t s);
+// The statistics of each row of a bf16 [rows][cols] matrix as one RowStat
+// slot (and the rows' pool slots if sl.out), and in the same launch the row
+// sums of w1t (bf16 [w1t_rows][cols]) -> colsum
+hipError_t launch_row_stats(const void* x, RowStat* stats, int32_t rows, int32_t cols, const void* w1t,
+                            float* colsum, int32_t w1t_rows, const RowSlots& sl, hipStream_t s);
 
 // Destinations of the bf16 f1 GEMM's output columns [U|V|Q|K].
 struct F1Args {
   void* uvqk;             // [M][4 inner]: U and Q always; K and V if kv_to_uvqk or no pools
   int32_t inner;
   bool kv_to_uvqk;
-  void* k_pool;           // paged K/V (nullptr: none), rows placed by RowInfo::pool_row
+  void* k_pool;           // paged K/V (nullptr: none), rows placed through the page table
   void* v_pool;
   int64_t pool_layer_offset;
   int32_t dh, page_size;
   void* s_out;            // optional [M][4 inner]: the pre-activation LayerNorm(x) . W1
+  float eps;
+  const int64_t* row_slots;   // [M] pool slot of each row (RowSlots::out), with k_pool
 };
-// [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row stats, routed per F1Args
-hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
+// [U|V|Q|K] = SiLU(LayerNorm(x) . W1) from raw x and its row statistics
+// (RowStat [M][slots]), routed per F1Args
+hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, const float* colsum, const void* w1t,
                           const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s);
 
 // Multitask ranking head on rows of y (bf16 [y_rows][d]): per task t and

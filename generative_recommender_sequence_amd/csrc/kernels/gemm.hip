@@ -16,12 +16,20 @@
 // are dealt to the 8 XCDs so that the n tiles of one m tile share an L2.
 //
 // Epilogue 0 applies the pre-norm algebraically: with mu, rstd the row
-// statistics of x and s_n = sum_k W1[k][n] (computed with the statistics),
+// statistics of x and s_n = sum_k W1[k][n] (computed once per weight set),
 //     LayerNorm(x) . W1 = rstd * (x . W1 - mu * s_n),
-// so x is multiplied as stored (no normalised copy).  The SiLU'd columns are
-// routed by chunk: U and Q to the token-major buffer, K and V either to the
-// same buffer (contiguous keys) or straight into their pages (paged cache; the
-// append of the new tokens).
+// so x is multiplied as stored (no normalised copy).  The statistics come as
+// per-share (mean, sum of squared deviations) slots, combined per row.  The
+// SiLU'd columns are routed by chunk: U and Q to the token-major buffer, K and
+// V either to the same buffer (contiguous keys) or straight into their pages
+// (paged cache; the append of the new tokens), at each row's pool slot, which
+// the row-statistics kernel of the stack's first layer looks up once for all
+// layers.
+//
+// Epilogue 1 may also leave the statistics of its output rows for the next
+// layer's pre-norm: per row and 128-column tile, the mean and the sum of
+// squared deviations of the stored (bf16-rounded) values, two-pass over the
+// registers, added across the two column waves in fixed order.
 //
 // Epilogue 2 is the multitask ranking head's hidden layer and output dot
 // product: A's rows are gathered through a row list, each column n gets
@@ -52,7 +60,10 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // Routing of f1's output columns (epilogue 0).
 struct F1Route {
-  const RowInfo* rows;        // [M] statistics and page slot of the input rows
+  const RowStat* stats;       // [M][stat_slots] statistics of the input rows
+  int32_t stat_slots;         // 1 .. kMaxStatSlots, dividing K
+  float eps;
+  const int64_t* row_slots;   // [M] pool slot of each row, or -1 (with k_pool)
   const float* colsum;        // [N] column sums of W1
   uint16_t* uvqk;             // [M][4 inner] token-major destination
   int32_t inner;              // H * dh
@@ -68,6 +79,7 @@ struct F1Route {
   const float* h_wout;        // [N] output weights
   float* h_partial;           // [M][N / BN] partial logits
   uint16_t* s_out;            // epilogue 0: the pre-activation x^ W1 [M][N] (nullptr: not kept)
+  RowStat* y_stats;           // epilogue 1: [M][N / BN] statistics of C's rows (nullptr: not kept)
 };
 
 template <int BM, int BN, int EPI>
@@ -165,7 +177,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) float cs_lds[EPI == 0 ? BN : 4];
   __shared__ __attribute__((aligned(16))) float hb_lds[EPI == 2 ? BN : 4];
   __shared__ __attribute__((aligned(16))) float hw_lds[EPI == 2 ? BN : 4];
-  RowInfo rinfo[MT];
+  RowStat rstat[MT][kMaxStatSlots];
+  int64_t slot[MT];
+  f32x4 cs_val;
   u32x2 resid[MT][NT][4];
   if (EPI == 2) {
     if (tid < BN / 4) {
@@ -173,10 +187,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       *reinterpret_cast<f32x4*>(&hw_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.h_wout[n0 + 4 * tid]);
     }
   } else if (EPI == 0) {
-    if (tid < BN / 4)
-      *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = *reinterpret_cast<const f32x4*>(&route.colsum[n0 + 4 * tid]);
+    // column sums: loaded here, stored to LDS after the first k step's copy is issued
+    cs_val = tid < BN / 4 ? *reinterpret_cast<const f32x4*>(&route.colsum[n0 + 4 * tid]) : f32x4{};
+    // straight-line loads (slots past stat_slots re-read the last one), so
+    // that none of them is waited for before the k loop's first barrier
 #pragma unroll
-    for (int i = 0; i < MT; ++i) rinfo[i] = route.rows[min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1)];
+    for (int i = 0; i < MT; ++i) {
+      const int m = min(m0 + wm * (BM / 2) + 32 * i + l32, M - 1);
+      const RowStat* sp = route.stats + static_cast<int64_t>(m) * route.stat_slots;
+#pragma unroll
+      for (int t = 0; t < kMaxStatSlots; ++t) rstat[i][t] = sp[min(t, route.stat_slots - 1)];
+      slot[i] = route.k_pool ? route.row_slots[m] : -1;
+    }
   } else if (EPI == 1) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -192,7 +214,29 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
 
   const int nk = K / GBK;
   copy_k(0, A0, B0);
-  __syncthreads();  // k step 0 in buffer 0
+  if (EPI == 0 && tid < BN / 4) *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = cs_val;
+  __syncthreads();  // k step 0 in buffer 0 (and the prefetched row records in)
+  // f1: each lane's row statistics
+  float mu[MT], rstd[MT];
+  if (EPI == 0) {
+    const float inv_slots = 1.0f / route.stat_slots, share = static_cast<float>(K) * inv_slots;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float mean = 0.f;
+#pragma unroll
+      for (int t = 0; t < kMaxStatSlots; ++t) mean += t < route.stat_slots ? rstat[i][t].mean : 0.f;
+      mean *= inv_slots;
+      float m2 = 0.f, dev = 0.f;
+#pragma unroll
+      for (int t = 0; t < kMaxStatSlots; ++t) {
+        const float dm = rstat[i][t].mean - mean;
+        m2 += t < route.stat_slots ? rstat[i][t].m2 : 0.f;
+        dev += t < route.stat_slots ? dm * dm : 0.f;
+      }
+      mu[i] = mean;
+      rstd[i] = __builtin_amdgcn_rsqf((m2 + share * dev) * (1.0f / K) + route.eps);
+    }
+  }
   for (int kt = 0; kt < nk; kt += 2) {
     if (kt + 1 < nk) copy_k((kt + 1) * GBK, A1, B1);
     __builtin_amdgcn_sched_barrier(0);  // issue the copy before this step's reads
@@ -236,13 +280,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   for (int i = 0; i < MT; ++i) {
     const int m = m0 + wm * (BM / 2) + 32 * i + l32;
     if (m >= M) continue;
-    float mu = 0.f, rstd = 1.f;
-    int64_t pool_row = -1;  // element offset of (page, head 0, slot) of row m, or -1
-    if (EPI == 0) {
-      mu = rinfo[i].mean;
-      rstd = rinfo[i].rstd;
-      if (route.k_pool && rinfo[i].pool_row >= 0) pool_row = route.pool_layer_offset + rinfo[i].pool_row;
-    }
+    // element offset of (page, head 0, slot) of row m in this layer, or -1
+    const int64_t pool_row = EPI == 0 && slot[i] >= 0 ? route.pool_layer_offset + slot[i] : -1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       // 32 columns starting at a multiple of 32: one chunk, one head (uniform)
@@ -265,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
           const f32x4 cs = *reinterpret_cast<const f32x4*>(&cs_lds[n - n0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            z[e] = rstd * (v[e] - mu * cs[e]);
+            z[e] = rstd[i] * (v[e] - mu[i] * cs[e]);
             v[e] = z[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[e] * -1.44269504088896340736f));
           }
         } else if (EPI == 1) {
@@ -279,6 +318,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
                               uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
         if (EPI == 1 || EPI == 3) {
           *reinterpret_cast<u32x2*>(C + static_cast<int64_t>(m) * N + n) = packed;
+          if (EPI == 1) {  // the stored values, for the row statistics
+            acc[i][j][4 * q + 0] = bf2f(packed[0] & 0xFFFFu);
+            acc[i][j][4 * q + 1] = bf2f(packed[0] >> 16);
+            acc[i][j][4 * q + 2] = bf2f(packed[1] & 0xFFFFu);
+            acc[i][j][4 * q + 3] = bf2f(packed[1] >> 16);
+          }
           continue;
         }
         if (EPI == 0 && route.s_out) {  // pre-activation tap (f1)
@@ -294,116 +339,109 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       }
     }
   }
-}
 
-// Per-row (mean, rstd) of x, two-pass from registers.  A wave takes
-// kRowsPerWave rows (their loads issued together) of one q-block, a block
-// kStatWaves waves (blockIdx = q-block * kStatGroups + row group), so the
-// q-block record is a block-uniform load and each row's page slot one
-// dependent load.  Blocks past the rows' blocks sum the rows of Wt (the column
-// sums of W1 that the f1 epilogue needs) unless the caller supplies them.
-// One row a wave measured best: more rows a wave leave too few waves for the
-// small batches.
-constexpr int kStatWaves = 4;
-constexpr int kRowsPerWave = 1;
-constexpr int kStatGroups = kBlockQ / (kStatWaves * kRowsPerWave);
-template <int kMaxChunks>  // cols <= 64 * 8 * kMaxChunks
-__global__ __launch_bounds__(64 * kStatWaves) void row_stats_kernel(const uint16_t* __restrict__ x,
-                                                                    RowInfo* __restrict__ info,
-                                                                    int32_t rows, int32_t cols,
-                                                                    float eps,
-                                                                    const uint16_t* __restrict__ wt,
-                                                                    float* __restrict__ colsum,
-                                                                    int32_t wt_rows, RowPages pg) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int stat_blocks = pg.n_qblocks * kStatGroups;
-  auto unpack = [](u32x4 raw, float* f) {
+  if (EPI == 1 && route.y_stats) {
+    // the row's 128 tile values: 2 x 32 per wave (lane halves g), two waves (wn)
+    __shared__ float part[2][2][EPI == 1 ? BM : 1];
+    float mean_t[MT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      f[e] = bf2f(static_cast<uint16_t>((e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu)));
-  };
-  if (static_cast<int>(blockIdx.x) >= stat_blocks) {
-    const int n0 = ((blockIdx.x - stat_blocks) * kStatWaves + wave) * kRowsPerWave;
-    u32x4 raw[kRowsPerWave][kMaxChunks];
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        const int col = 8 * (lane + 64 * c);
-        raw[r][c] = (n0 + r < wt_rows && col < cols)
-                        ? *reinterpret_cast<const u32x4*>(wt + static_cast<int64_t>(n0 + r) * cols + col)
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
+    for (int i = 0; i < MT; ++i) {
       float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        float f[8];
-        unpack(raw[r][c], f);
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += f[e];
-      }
-      s = wave_sum(s);
-      if (lane == 0 && n0 + r < wt_rows) colsum[n0 + r] = s;
+        for (int e = 0; e < 16; ++e) s += acc[i][j][e];
+      s += __shfl_xor(s, 32);
+      if (g == 0) part[0][wn][wm * (BM / 2) + 32 * i + l32] = s;
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int rl = wm * (BM / 2) + 32 * i + l32;
+      mean_t[i] = (part[0][0][rl] + part[0][1][rl]) * (1.0f / BN);
+      float q2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float dv = acc[i][j][e] - mean_t[i];
+          q2 += dv * dv;
+        }
+      q2 += __shfl_xor(q2, 32);
+      if (g == 0) part[1][wn][rl] = q2;
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < M)
+      route.y_stats[static_cast<int64_t>(m0 + tid) * (N / BN) + n0 / BN] =
+          RowStat{(part[0][0][tid] + part[0][1][tid]) * (1.0f / BN), part[1][0][tid] + part[1][1][tid]};
+  }
+}
+
+// Per-row (mean, sum of squared deviations) of x, two-pass from registers,
+// one row a wave, kStatWaves waves a block.  Blocks past the rows' blocks sum
+// the rows of Wt (the column sums of W1 that the f1 epilogue needs) unless the
+// caller supplies them.
+constexpr int kStatWaves = 4;
+template <int kMaxChunks>  // cols <= 64 * 8 * kMaxChunks
+__global__ __launch_bounds__(64 * kStatWaves) void row_stats_kernel(const uint16_t* __restrict__ x,
+                                                                    RowStat* __restrict__ stats,
+                                                                    int32_t rows, int32_t cols,
+                                                                    const uint16_t* __restrict__ wt,
+                                                                    float* __restrict__ colsum,
+                                                                    int32_t wt_rows, RowSlots sl) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stat_blocks = (rows + kStatWaves - 1) / kStatWaves;
+  const bool is_wt = static_cast<int>(blockIdx.x) >= stat_blocks;
+  const int r = (is_wt ? static_cast<int>(blockIdx.x) - stat_blocks : static_cast<int>(blockIdx.x)) * kStatWaves + wave;
+  if (r >= (is_wt ? wt_rows : rows)) return;
+  const uint16_t* src = (is_wt ? wt : x) + static_cast<int64_t>(r) * cols;
+  u32x4 raw[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int col = 8 * (lane + 64 * c);
+    raw[c] = col < cols ? *reinterpret_cast<const u32x4*>(src + col) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (!is_wt && sl.out && lane == 0) {
+    // the row's page slot: its (user, position), then the page table
+    const RowPos rp = sl.row_pos[r];
+    const int lp = rp.pos / sl.page_size;
+    int64_t off = -1;
+    if (lp < sl.max_pages) {
+      const int page = sl.page_table[static_cast<int64_t>(rp.user) * sl.max_pages + lp];
+      if (page >= 0 && page < sl.num_pages)
+        off = (static_cast<int64_t>(page) * sl.H * sl.page_size + (rp.pos - lp * sl.page_size)) * sl.dh;
+    }
+    sl.out[r] = off;
+  }
+  float v[kMaxChunks * 8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[8 * c + e] = bf2f(static_cast<uint16_t>((e & 1) ? (raw[c][e >> 1] >> 16) : (raw[c][e >> 1] & 0xFFFFu)));
+      s += v[8 * c + e];
+    }
+  s = wave_sum(s);
+  if (is_wt) {
+    if (lane == 0) colsum[r] = s;
     return;
   }
-  const QBlock qb = pg.qblocks[blockIdx.x / kStatGroups];
-  const int l0 = ((blockIdx.x % kStatGroups) * kStatWaves + wave) * kRowsPerWave;
-  if (l0 >= qb.count) return;
-  u32x4 raw[kRowsPerWave][kMaxChunks];
+  const float mean = s / cols;
+  float q = 0.f;
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (8 * (lane + 64 * c) < cols) {
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int col = 8 * (lane + 64 * c);
-      raw[r][c] = (l0 + r < qb.count && col < cols)
-                      ? *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(qb.row0 + l0 + r) * cols + col)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-  // the page slot each new token's K/V rows go to (-1: none)
-  int64_t pool_row[kRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    pool_row[r] = -1;
-    if (pg.page_table && l0 + r < qb.count) {
-      const int pos = qb.pos0 + l0 + r;
-      const int lp = pos / pg.page_size;
-      if (lp < pg.max_pages) {
-        const int page = pg.page_table[static_cast<int64_t>(qb.user) * pg.max_pages + lp];
-        if (page >= 0 && page < pg.num_pages)
-          pool_row[r] = (static_cast<int64_t>(page) * pg.H * pg.page_size + (pos - lp * pg.page_size)) * pg.dh;
+      for (int e = 0; e < 8; ++e) {
+        const float dv = v[8 * c + e] - mean;
+        q += dv * dv;
       }
     }
   }
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    if (l0 + r >= qb.count) break;
-    float v[kMaxChunks * 8];
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      unpack(raw[r][c], &v[8 * c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[8 * c + e];
-    }
-    const float mean = wave_sum(s) / cols;
-    float q = 0.f;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (8 * (lane + 64 * c) < cols) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dv = v[8 * c + e] - mean;
-          q += dv * dv;
-        }
-      }
-    }
-    const float rstd = 1.0f / sqrtf(wave_sum(q) / cols + eps);
-    if (lane == 0) info[qb.row0 + l0 + r] = RowInfo{mean, rstd, pool_row[r]};
-  }
+  q = wave_sum(q);
+  if (lane == 0) stats[r] = RowStat{mean, q};
 }
 
 constexpr int FT = 64, FK = 16;
@@ -463,21 +501,21 @@ __global__ __launch_bounds__(256) void head_finalize_kernel(const float* __restr
 
 }  // namespace
 
-hipError_t launch_row_stats(const void* x, RowInfo* info, int32_t rows, int32_t cols, float eps,
-                            const void* w1t, float* colsum, int32_t w1t_rows, const RowPages& pg,
-                            hipStream_t s) {
+hipError_t launch_row_stats(const void* x, RowStat* stats, int32_t rows, int32_t cols, const void* w1t,
+                            float* colsum, int32_t w1t_rows, const RowSlots& sl, hipStream_t s) {
   if (rows == 0 && w1t_rows == 0) return hipSuccess;
   if (cols % 8 != 0 || cols > 64 * 8 * 4) return hipErrorInvalidValue;
-  const int per_block = kStatWaves * kRowsPerWave;
-  const int blocks = pg.n_qblocks * kStatGroups + (w1t_rows + per_block - 1) / per_block;
+  if (sl.out && (!sl.row_pos || !sl.page_table || sl.page_size <= 0 || sl.max_pages <= 0))
+    return hipErrorInvalidValue;
+  const int blocks = (rows + kStatWaves - 1) / kStatWaves + (w1t_rows + kStatWaves - 1) / kStatWaves;
   if (cols <= 64 * 8)
     hipLaunchKernelGGL(row_stats_kernel<1>, dim3(blocks), dim3(64 * kStatWaves), 0, s,
-                       static_cast<const uint16_t*>(x), info, rows, cols, eps,
-                       static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
+                       static_cast<const uint16_t*>(x), stats, rows, cols, static_cast<const uint16_t*>(w1t),
+                       colsum, w1t_rows, sl);
   else
     hipLaunchKernelGGL(row_stats_kernel<4>, dim3(blocks), dim3(64 * kStatWaves), 0, s,
-                       static_cast<const uint16_t*>(x), info, rows, cols, eps,
-                       static_cast<const uint16_t*>(w1t), colsum, w1t_rows, pg);
+                       static_cast<const uint16_t*>(x), stats, rows, cols, static_cast<const uint16_t*>(w1t),
+                       colsum, w1t_rows, sl);
   return hipGetLastError();
 }
 
@@ -487,13 +525,18 @@ static unsigned gemm_grid(int32_t M, int32_t N) {
   return (tiles + 7u) / 8u * 8u;  // a multiple of the 8 XCDs
 }
 
-hipError_t launch_f1_bf16(const void* x, const RowInfo* info, const float* colsum, const void* w1t,
+hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, const float* colsum, const void* w1t,
                           const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s) {
   if (M == 0) return hipSuccess;
   constexpr int BM = 128, BN = 128;
   if (N % BN != 0 || K % GBK != 0 || f.inner % 32 != 0 || f.dh % 32 != 0) return hipErrorInvalidValue;
+  if (slots < 1 || slots > kMaxStatSlots || K % slots != 0) return hipErrorInvalidValue;
+  if (f.k_pool && !f.row_slots) return hipErrorInvalidValue;
   F1Route r{};
-  r.rows = info;
+  r.stats = stats;
+  r.stat_slots = slots;
+  r.eps = f.eps;
+  r.row_slots = f.row_slots;
   r.colsum = colsum;
   r.uvqk = static_cast<uint16_t*>(f.uvqk);
   r.inner = f.inner;
@@ -538,23 +581,27 @@ hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, void* C,
-                       const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s) {
+                       const void* R, int32_t M, int32_t N, int32_t K, hipStream_t s, RowStat* y_stats) {
   if (M == 0) return hipSuccess;
   if (dtype == HSTU_BF16) {
     // bf16: f2 (+ residual, epilogue 1) and the backward's plain products
     // (epilogue 3); f1 goes through launch_f1_bf16
     constexpr int BM = 64, BN = 128;
     if ((epilogue != 1 && epilogue != 3) || N % BN != 0 || K % GBK != 0) return hipErrorInvalidValue;
-    if (epilogue == 1)
+    if (y_stats && epilogue != 1) return hipErrorInvalidValue;
+    if (epilogue == 1) {
+      F1Route r{};
+      r.y_stats = y_stats;
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
                          static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
-                         static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), F1Route{}, M, N,
-                         K);
-    else
+                         static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), r, M, N, K);
+    } else {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 3>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
                          static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
                          static_cast<uint16_t*>(C), nullptr, F1Route{}, M, N, K);
+    }
   } else {
+    if (y_stats) return hipErrorInvalidValue;
     dim3 grid((N + FT - 1) / FT, (M + FT - 1) / FT);
     auto a = static_cast<const float*>(A);
     auto b = static_cast<const float*>(Bm);

@@ -59,7 +59,8 @@ class hstu_layer_args(ctypes.Structure):
                 ("y", c_vp), ("w1", c_vp), ("w2", c_vp), ("rab", c_vp), ("num_buckets", c_i32),
                 ("cache", c_vp), ("layer", c_i32), ("d_page_table", c_vp), ("workspace", c_vp),
                 ("workspace_bytes", c_size), ("uvqk_out", c_vp), ("o_out", c_vp), ("g_out", c_vp),
-                ("s_out", c_vp), ("w1_colsum", c_vp)]
+                ("s_out", c_vp), ("w1_colsum", c_vp),
+                ("x_stats", c_vp), ("y_stats", c_vp), ("row_slots", c_vp)]
 
 
 class hstu_layer_bwd_args(ctypes.Structure):

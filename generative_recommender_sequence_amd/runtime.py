@@ -257,10 +257,25 @@ def layer_args(model: Model, req: Request, li: int, x: torch.Tensor, y: torch.Te
     return a
 
 
-def workspace_for(model: Model, req: Request, device="cuda") -> torch.Tensor:
+def _layer_ws_bytes(model: Model, req: Request) -> int:
     a = hstu.hstu_layer_args()
     a.dtype, a.d_model, a.plan = model.dtype, model.d_model, req.plan
-    n = hstu.hstu_layer_workspace_size(a)
+    return hstu.hstu_layer_workspace_size(a)
+
+
+def _stats_bytes(model: Model, n_new: int) -> int:
+    """One buffer of row statistics that f2 hands to the next layer's pre-norm
+    (bf16, d_model <= 512): [n_new][d_model / 128] (mean, M2) pairs; the rows'
+    pool slots (int64 [n_new]) take no more."""
+    if model.dtype != hstu.HSTU_BF16 or model.d_model > 512:
+        return 0
+    return -(-(n_new * max(model.d_model // 128, 1) * 8) // 256) * 256
+
+
+def workspace_for(model: Model, req: Request, device="cuda") -> torch.Tensor:
+    """The layer workspace followed by two row-statistics buffers (ping-pong
+    between the layers of a stack) and the rows' pool slots."""
+    n = _layer_ws_bytes(model, req) + 3 * _stats_bytes(model, int(req.info.n_new_total))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -269,18 +284,34 @@ def forward(model: Model, req: Request, x: torch.Tensor, cache: Optional[PagedCa
             taps: Optional[List[dict]] = None, stream=None,
             out_bufs: Optional[List[torch.Tensor]] = None) -> torch.Tensor:
     """Runs the stack on the new tokens x [N_new, d] in one native call
-    (hstu_stack_forward); returns the last layer's y (one of out_bufs)."""
+    (hstu_stack_forward); layer k writes out_bufs[k % len(out_bufs)] (two
+    buffers by default) and the last layer's y is returned.  Each layer's f2
+    leaves the row statistics of its y for the next layer's pre-norm when the
+    workspace has room for them."""
     s = stream_handle(stream)
     if workspace is None:
         workspace = workspace_for(model, req, x.device)
     layers = list(range(model.num_layers)) if layers is None else list(layers)
     if out_bufs is None:
         out_bufs = [torch.empty_like(x), torch.empty_like(x)]
+    lw, sb = _layer_ws_bytes(model, req), _stats_bytes(model, x.shape[0])
+    stats = None
+    if sb and len(layers) > 1 and workspace.numel() >= lw + 3 * sb:
+        base = workspace.data_ptr() + lw
+        stats = [base, base + sb, base + 2 * sb]   # y/x statistics ping-pong, pool slots
     cur = x
     args = []
     for k, li in enumerate(layers):
-        out = out_bufs[k % 2]
-        args.append(layer_args(model, req, li, cur, out, cache, workspace, taps[k] if taps else None))
+        out = out_bufs[k % len(out_bufs)]
+        a = layer_args(model, req, li, cur, out, cache, workspace, taps[k] if taps else None)
+        if stats is not None:
+            a.workspace_bytes = lw
+            a.row_slots = stats[2]
+            if k > 0:
+                a.x_stats = stats[(k - 1) % 2]
+            if k + 1 < len(layers):
+                a.y_stats = stats[k % 2]
+        args.append(a)
         cur = out
     hstu.hstu_stack_forward(args, s)
     return cur

@@ -317,6 +317,23 @@ typedef struct {
   /* optional (bf16): W1's column sums from hstu_w1_colsum for these weights
    * (device fp32 [4*H*dh]); NULL: computed in every call */
   const float *w1_colsum;
+  /* optional (bf16, d_model <= 512): row statistics of a stack's
+   * activations, so that a layer's pre-norm needs no pass of its own over x.
+   * Layout: device fp32 [n_new_total][d_model/128][2]; entry (r, t) holds the
+   * mean and the sum of squared deviations from it of row r's columns
+   * 128 t .. 128 t + 127, as stored (bf16-rounded).  y_stats (NULL = skip)
+   * receives those of y; x_stats (NULL: this call computes them) must hold
+   * those of x, as the previous layer's y_stats does.  Neither may overlap
+   * x, y or the workspace. */
+  const float *x_stats;
+  float *y_stats;
+  /* optional (bf16, paged plan): device int64 [n_new_total], where each
+   * new-token row's K/V go within one layer of the pools (the element offset
+   * of its (page, head 0, slot); -1: not appended).  The same for every
+   * layer of one request: a call without x_stats writes it, a call with
+   * x_stats on a paged plan requires it and reads it (so the page table must
+   * not change between the layers of a request). */
+  int64_t *row_slots;
 } hstu_layer_args;
 
 /* The column sums of W1 that the bf16 layer's fused pre-norm uses (the sum

@@ -69,24 +69,23 @@ def pool_rows(cache: runtime.PagedCache, which: str, layer: int, pt_row, start: 
 
 
 def run_layers_with_taps(scn: runtime.Scenario, req, x: torch.Tensor):
-    """Runs the stack layer by layer with taps; returns per-layer dicts of
-    device tensors (x, y, uvqk, o, g)."""
+    """Runs the stack in one call, as the product does (so each layer's
+    pre-norm takes the row statistics the layer before left), with taps and
+    one output buffer per layer; returns per-layer dicts of device tensors
+    (x, y, uvqk, o, g)."""
     model = scn.model
     inner = model.num_heads * model.head_dim
     n = x.shape[0]
     t = runtime.tdtype(model.dtype)
     ws = runtime.workspace_for(model, req, x.device)
-    out = []
-    cur = x
-    for li in range(model.num_layers):
-        taps = {"uvqk": torch.empty((n, 4 * inner), dtype=t, device=x.device),
-                "o": torch.empty((n, inner), dtype=torch.float32, device=x.device),
-                "g": torch.empty((n, inner), dtype=t, device=x.device)}
-        y = runtime.forward(model, req, cur, scn.cache, ws, layers=[li], taps=[taps])
-        out.append(dict(x=cur, y=y, **taps))
-        cur = y
+    taps = [{"uvqk": torch.empty((n, 4 * inner), dtype=t, device=x.device),
+             "o": torch.empty((n, inner), dtype=torch.float32, device=x.device),
+             "g": torch.empty((n, inner), dtype=t, device=x.device)} for _ in range(model.num_layers)]
+    ys = [torch.empty_like(x) for _ in range(model.num_layers)]
+    runtime.forward(model, req, x, scn.cache, ws, taps=taps, out_bufs=ys)
     torch.cuda.synchronize()
-    return out
+    xs = [x] + ys[:-1]
+    return [dict(x=xs[li], y=ys[li], **taps[li]) for li in range(model.num_layers)]
 
 
 def check_layers(scn: runtime.Scenario, req, per_layer, sample, label="") -> dict:

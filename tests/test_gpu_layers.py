@@ -155,3 +155,62 @@ def test_precomputed_w1_colsum_is_identical():
     torch.cuda.synchronize()
     assert saved[0] is not None and torch.equal(y1, y2)
     req.close()
+
+
+def test_f2_row_statistics_slots():
+    """f2's row statistics of y (mean and sum of squared deviations per
+    128-column tile of the stored bf16 y) against float64 sums over the
+    returned y, and the combined slots against one pass over the row."""
+    from generative_recommender_sequence_amd import hstu
+    say("f2 row statistics")
+    w = _small("hit", "bf16", hist=[200, 33, 5], T=16, layers=1)
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    req, x = scn.make_request()
+    model = scn.model
+    n, d = x.shape
+    slots = d // 128
+    ws = runtime.workspace_for(model, req, x.device)
+    y = torch.empty_like(x)
+    stats = torch.full((n, slots, 2), float("nan"), dtype=torch.float32, device=x.device)
+    a = runtime.layer_args(model, req, 0, x, y, scn.cache, ws)
+    a.y_stats = stats.data_ptr()
+    hstu.hstu_stack_forward([a], runtime.stream_handle())
+    torch.cuda.synchronize()
+    yt = to64(y).reshape(n, slots, 128)
+    mean = yt.mean(axis=2)
+    m2 = ((yt - mean[..., None]) ** 2).sum(axis=2)
+    got = stats.cpu().numpy().astype(np.float64)
+    e_mean = np.max(np.abs(got[..., 0] - mean)) / max(np.max(np.abs(yt)), 1e-30)
+    e_m2 = np.max(np.abs(got[..., 1] - m2) / np.maximum(m2, 1e-30))
+    say(f"  mean err {e_mean:.2e}  M2 rel err {e_m2:.2e}")
+    assert e_mean < 1e-6 and e_m2 < 1e-5
+    # the next layer's input statistics from slots equal those of one pass
+    full_mean = yt.reshape(n, d).mean(axis=1)
+    comb_mean = got[..., 0].mean(axis=1)
+    comb_m2 = got[..., 1].sum(axis=1) + 128 * ((got[..., 0] - comb_mean[:, None]) ** 2).sum(axis=1)
+    full_m2 = ((yt.reshape(n, d) - full_mean[:, None]) ** 2).sum(axis=1)
+    assert np.max(np.abs(comb_m2 - full_m2) / full_m2) < 1e-5
+    # a paged layer given x_stats must be given the rows' pool slots as well
+    b = runtime.layer_args(model, req, 0, y, x.clone(), scn.cache, ws)
+    b.x_stats = stats.data_ptr()
+    with pytest.raises(RuntimeError, match="needs row_slots"):
+        hstu.hstu_stack_forward([b], runtime.stream_handle())
+    req.close()
+
+
+def test_row_statistics_need_narrow_bf16():
+    """x_stats / y_stats are refused for d_model above 512."""
+    from generative_recommender_sequence_amd import hstu
+    cfg = small_config(dtype="bf16", d_model=1024, num_heads=2, head_dim=128, num_layers=1, n_targets=8)
+    w = generate(cfg, 4, batch=2, hist_override=[40, 20])
+    scn = runtime.Scenario(w)
+    req, x = scn.make_request()
+    ws = runtime.workspace_for(scn.model, req, x.device)
+    y = torch.empty_like(x)
+    stats = torch.empty((x.shape[0], 8, 2), dtype=torch.float32, device=x.device)
+    a = runtime.layer_args(scn.model, req, 0, x, y, None, ws)
+    a.y_stats = stats.data_ptr()
+    with pytest.raises(RuntimeError, match="d_model <= 512"):
+        hstu.hstu_stack_forward([a], runtime.stream_handle())
+    req.close()
