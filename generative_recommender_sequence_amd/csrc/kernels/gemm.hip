@@ -12,8 +12,10 @@
 // 64 k wide with a 16-byte-chunk XOR swizzle that keeps the 16-lane operand
 // reads free of bank conflicts.  Each MFMA multiplies a Wt fragment by an x
 // fragment, producing C^T tiles, so a lane owns 4 consecutive output columns
-// of one row and stores (and reads the residual) 8 bytes at a time.  Blocks
-// are dealt to the 8 XCDs so that the n tiles of one m tile share an L2.
+// of one row (and reads the residual 8 bytes at a time).  The finished tile
+// goes through LDS (the freed operand buffers) so that whole 256-byte rows
+// leave in 16-byte stores.  Blocks are dealt to the 8 XCDs so that the n
+// tiles of one m tile share an L2.
 //
 // Epilogue 0 applies the pre-norm algebraically: with mu, rstd the row
 // statistics of x and s_n = sum_k W1[k][n] (computed once per weight set),
@@ -275,33 +277,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     return;
   }
 
-  // epilogue: lane owns row m = ... + l32 and columns n = ... + 8 (r/4) + 4 g + [0, 4)
+  // epilogue, phase 1: each lane finishes its values (row m = ... + l32,
+  // columns n = ... + 8 (r/4) + 4 g + [0, 4)) and writes them as bf16 into an
+  // LDS image of the output tile, in the operand buffers the k loop has
+  // released: rows 0-63 in A0 and 64-127 in B0 (BM = 128), all rows in B0
+  // (BM = 64).  The 16-byte chunk c of local row r sits at slot c ^ (r & 15).
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  auto stage_row = [&](int r) -> lds_u16* {
+    if (BM == 128) return r < 64 ? A0 + r * BN : B0 + (r - 64) * BN;
+    return B0 + r * BN;
+  };
+  __shared__ int64_t slot_lds[EPI == 0 ? BM : 1];  // pool offset of each local row, or -1
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int m = m0 + wm * (BM / 2) + 32 * i + l32;
+    const int rl = wm * (BM / 2) + 32 * i + l32;
+    const int m = m0 + rl;
     if (m >= M) continue;
-    // element offset of (page, head 0, slot) of row m in this layer, or -1
-    const int64_t pool_row = EPI == 0 && slot[i] >= 0 ? route.pool_layer_offset + slot[i] : -1;
+    if (EPI == 0 && wn == 0 && g == 0)
+      slot_lds[rl] = route.k_pool && slot[i] >= 0 ? route.pool_layer_offset + slot[i] : -1;
+    lds_u16* const srow = stage_row(rl);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      // 32 columns starting at a multiple of 32: one chunk, one head (uniform)
-      const int nb = n0 + wn * (BN / 2) + 32 * j;
-      const int chunk = EPI == 0 ? nb / route.inner : 0;  // 0 U, 1 V, 2 Q, 3 K
-      const int cb = nb - chunk * route.inner;
-      const int h = EPI == 0 ? cb / route.dh : 0;
-      const int e0 = cb - h * route.dh;
-      const bool is_kv = EPI == 0 && (chunk == 1 || chunk == 3);
-      const bool to_uvqk = EPI == 0 && (!is_kv || route.kv_to_uvqk || !route.k_pool);
-      const bool to_pool = is_kv && pool_row >= 0;
-      uint16_t* pool = chunk == 3 ? route.k_pool : route.v_pool;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nb + 8 * q + 4 * g;  // first of this lane's 4 columns
+        const int nl = wn * (BN / 2) + 32 * j + 8 * q + 4 * g;  // first of this lane's 4 columns
         float v[4], z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
         if (EPI == 0) {
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(&cs_lds[n - n0]);
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(&cs_lds[nl]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             z[e] = rstd[i] * (v[e] - mu[i] * cs[e]);
@@ -316,26 +321,55 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
         }
         const u32x2 packed = {uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16),
                               uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
-        if (EPI == 1 || EPI == 3) {
-          *reinterpret_cast<u32x2*>(C + static_cast<int64_t>(m) * N + n) = packed;
-          if (EPI == 1) {  // the stored values, for the row statistics
-            acc[i][j][4 * q + 0] = bf2f(packed[0] & 0xFFFFu);
-            acc[i][j][4 * q + 1] = bf2f(packed[0] >> 16);
-            acc[i][j][4 * q + 2] = bf2f(packed[1] & 0xFFFFu);
-            acc[i][j][4 * q + 3] = bf2f(packed[1] >> 16);
-          }
-          continue;
+        if (EPI == 1) {  // the stored values, for the row statistics
+          acc[i][j][4 * q + 0] = bf2f(packed[0] & 0xFFFFu);
+          acc[i][j][4 * q + 1] = bf2f(packed[0] >> 16);
+          acc[i][j][4 * q + 2] = bf2f(packed[1] & 0xFFFFu);
+          acc[i][j][4 * q + 3] = bf2f(packed[1] >> 16);
         }
-        if (EPI == 0 && route.s_out) {  // pre-activation tap (f1)
+        if (EPI == 0 && route.s_out) {  // pre-activation tap (f1), stored directly
           const u32x2 pre = {uint32_t(f2bf(z[0])) | (uint32_t(f2bf(z[1])) << 16),
                              uint32_t(f2bf(z[2])) | (uint32_t(f2bf(z[3])) << 16)};
-          *reinterpret_cast<u32x2*>(route.s_out + static_cast<int64_t>(m) * N + n) = pre;
+          *reinterpret_cast<u32x2*>(route.s_out + static_cast<int64_t>(m) * N + n0 + nl) = pre;
         }
-        if (to_uvqk) *reinterpret_cast<u32x2*>(route.uvqk + static_cast<int64_t>(m) * N + n) = packed;
-        if (to_pool) {
-          const int64_t off = pool_row + static_cast<int64_t>(h) * route.page_size * route.dh + e0 + 8 * q + 4 * g;
-          *reinterpret_cast<u32x2*>(pool + off) = packed;
-        }
+        *(lds_u32x2*)(srow + 8 * ((nl >> 3) ^ (rl & 15)) + 4 * g) = packed;
+      }
+    }
+  }
+  __syncthreads();
+
+  // phase 2: whole rows out, 4 rows an instruction (16 lanes x 16 bytes a
+  // row).  A tile is one head of one chunk of [U|V|Q|K] (f1 checks that the
+  // tile width is the head size), so its routing is block-uniform.
+  {
+    const int crow = lane >> 4, cch = lane & 15;
+    constexpr int RPW = BM / 4;  // rows per wave
+    int chunk = 0, h = 0;
+    if (EPI == 0) {
+      chunk = n0 / route.inner;  // 0 U, 1 V, 2 Q, 3 K
+      h = (n0 - chunk * route.inner) / route.dh;
+    }
+    const bool is_kv = EPI == 0 && route.k_pool && (chunk == 1 || chunk == 3);
+    const bool to_uvqk = EPI == 0 && (!is_kv || route.kv_to_uvqk);
+    uint16_t* const pool = chunk == 3 ? route.k_pool : route.v_pool;
+    const int64_t head_off = static_cast<int64_t>(h) * route.page_size * route.dh;
+#pragma unroll
+    for (int it = 0; it < RPW / 4; ++it) {
+      const int rl = wave * RPW + 4 * it + crow;
+      const int m = m0 + rl;
+      if (m >= M) continue;
+      const u32x4 val = *(const lds_u32x4*)(stage_row(rl) + 8 * (cch ^ (rl & 15)));
+      if (EPI == 1 || EPI == 3) {
+        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(m) * N + n0 + 8 * cch) = val;
+        continue;
+      }
+      // f1's output streams past the L2 (non-temporal): it is not re-read by
+      // this launch, and evicting W1 and the x rows for it cost more
+      if (to_uvqk)
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(route.uvqk + static_cast<int64_t>(m) * N + n0 + 8 * cch));
+      if (is_kv) {
+        const int64_t pr = slot_lds[rl];
+        if (pr >= 0) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(pool + pr + head_off + 8 * cch));
       }
     }
   }
@@ -529,7 +563,8 @@ hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, co
                           const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s) {
   if (M == 0) return hipSuccess;
   constexpr int BM = 128, BN = 128;
-  if (N % BN != 0 || K % GBK != 0 || f.inner % 32 != 0 || f.dh % 32 != 0) return hipErrorInvalidValue;
+  // a 128-column tile is one head of one chunk
+  if (N % BN != 0 || K % GBK != 0 || f.dh != BN || f.inner % BN != 0) return hipErrorInvalidValue;
   if (slots < 1 || slots > kMaxStatSlots || K % slots != 0) return hipErrorInvalidValue;
   if (f.k_pool && !f.row_slots) return hipErrorInvalidValue;
   F1Route r{};
