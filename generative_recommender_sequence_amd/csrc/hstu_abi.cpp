@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <numeric>
+#include <tuple>
 
 #include "internal.h"
 
@@ -280,16 +281,21 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     }
   }
   p->n_slots = slot;
-  // Dispatch order.  Pieces of one (user, head) read the same K/V, so they
-  // go to one XCD and run there together, sharing its L2.  Groups are dealt
-  // to XCDs largest first onto the least-loaded one; inside an XCD, groups
-  // and pieces run longest first.  Block b runs on XCD b % 8, so XCD x's
-  // k-th piece sits at index 8k + x; short queues are padded with no-op
-  // entries (slot -1).
+  // Dispatch order.  Block b runs on XCD b % 8, and each XCD starts its
+  // next block as soon as one of its slots frees, independently of the
+  // others, so the launch ends when the most loaded XCD drains.  Pieces of
+  // one (user, head) read the same K/V and go to one XCD where the balance
+  // allows, sharing its L2: groups are taken largest first, each onto the
+  // least-loaded XCD, and a piece that would lift that XCD above an equal
+  // share of all tiles goes to the least-loaded XCD instead.  Each XCD then
+  // runs its pieces longest first (ties keep the group order), so that its
+  // last slots free together; XCD x's k-th piece sits at index 8k + x and
+  // short queues are padded with no-op entries (slot -1).
   {
     std::vector<std::vector<std::pair<int32_t, WorkItem>>> groups;
     std::vector<int64_t> gcost;
     std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1);
+    int64_t all = 0;
     for (const auto& pc : pieces) {
       int32_t key = pc.second.user * H + pc.second.head;
       if (gid[key] < 0) {
@@ -299,27 +305,40 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
       }
       groups[gid[key]].push_back(pc);
       gcost[gid[key]] += pc.first;
+      all += pc.first;
     }
+    const int64_t share = (all + kXcds - 1) / kXcds;
     std::vector<int32_t> gorder(groups.size());
     std::iota(gorder.begin(), gorder.end(), 0);
     std::stable_sort(gorder.begin(), gorder.end(),
                      [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
-    std::vector<std::vector<WorkItem>> q(kXcds);
+    // (visible tiles, arrival order, item) per XCD
+    std::vector<std::vector<std::tuple<int32_t, int32_t, WorkItem>>> q(kXcds);
     std::vector<int64_t> load(kXcds, 0);
+    int32_t seq = 0;
+    auto least = [&]() { return static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin()); };
     for (int32_t gi : gorder) {
-      int x = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
       auto& grp = groups[gi];
       std::stable_sort(grp.begin(), grp.end(),
                        [](const auto& a, const auto& b) { return a.first > b.first; });
-      for (const auto& pc : grp) q[x].push_back(pc.second);
-      load[x] += gcost[gi];
+      const int home = least();
+      for (const auto& pc : grp) {
+        const int x = load[home] + pc.first <= share ? home : least();
+        q[x].emplace_back(pc.first, seq++, pc.second);
+        load[x] += pc.first;
+      }
     }
     size_t depth = 0;
-    for (const auto& qq : q) depth = std::max(depth, qq.size());
+    for (auto& qq : q) {
+      std::sort(qq.begin(), qq.end(), [](const auto& a, const auto& b) {
+        return std::get<0>(a) != std::get<0>(b) ? std::get<0>(a) > std::get<0>(b) : std::get<1>(a) < std::get<1>(b);
+      });
+      depth = std::max(depth, qq.size());
+    }
     WorkItem pad{};
     pad.slot = -1;
     for (size_t k = 0; k < depth; ++k)
-      for (int x = 0; x < kXcds; ++x) p->items.push_back(k < q[x].size() ? q[x][k] : pad);
+      for (int x = 0; x < kXcds; ++x) p->items.push_back(k < q[x].size() ? std::get<2>(q[x][k]) : pad);
   }
 
   // packed device image
