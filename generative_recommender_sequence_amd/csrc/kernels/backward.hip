@@ -345,9 +345,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ p
 // Each wave owns 32 keys; a step covers 64 queries as two 32-query halves
 // whose products are issued together, so one half's SiLU work overlaps the
 // other half's MFMAs.  The rab gradient is summed per distance i - j in LDS
-// (an atomic add per visible pair, at most two lanes on one address; a wave
-// whose 32 x 32 pairs all fall in one bucket adds one wave sum), then folded
-// into buckets, and written as this item's partial.
+// (a wave gathers its 32 x 32 pairs by distance across lanes and adds one
+// atomic per distance; a wave whose pairs fall in at most four buckets adds
+// one wave sum per bucket), then folded into buckets, and written as this
+// item's partial.
 constexpr int KB = 128;        // keys per item (4 waves x 32)
 constexpr int QT = 64;         // queries per step
 constexpr int kTab = QT + KB;  // distances per step (191 used)
@@ -359,7 +360,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   __shared__ __attribute__((aligned(16))) uint16_t D1s[QT * DH];
   __shared__ float bias0[kTab], bias1[kTab];
   __shared__ float drab_s[256];
-  extern __shared__ float dist_s[];  // [max_len + 64]: sum of dz per distance, then a spare slot per lane
+  __shared__ float diag_s[4 * 32 * 33];  // per-wave scratch of the distance sums
+  extern __shared__ float dist_s[];  // [max_len + 64]: sum of dz per distance (the last 64 unused)
   lds_u16* const Q0 = (lds_u16*)Q0s;
   lds_u16* const D0 = (lds_u16*)D0s;
   lds_u16* const Q1 = (lds_u16*)Q1s;
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   const int wave = uniform(tid >> 6);
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
-  const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur; then 64 spare slots
+  const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur
   for (int i = tid; i < nb; i += 256) drab_s[i] = 0.f;
   for (int i = tid; i < ndist + 64; i += 256) dist_s[i] = 0.f;
   // this wave's keys as B operands (K for S = Q K^T, V for dP = dO V^T)
@@ -431,12 +433,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
     for (int s = 0; s < DH / 16; ++s) qaddr[s] = row * DH + 8 * ((2 * s + g) ^ swz(row));
   }
 
+  // Per-distance sums of a half's dz (register r of lane (l, g) holds key
+  // offset l and query offset 16 (r / 8) + 8 g + r % 8, at distance D + that
+  // offset - l, D = qh - kw0): the wave writes its 32 x 32 tile to its own
+  // LDS scratch, each lane sums one diagonal (query offset - key offset =
+  // lane - 31) and adds it with a single LDS atomic.  Float LDS atomics are
+  // slow on this chip: one per pair cost more than the rest of the step.
+  // The scratch is private to the wave and a wave's LDS operations complete
+  // in order, so no barrier is needed between the writes and the reads.
+  float* const scr = diag_s + wave * (32 * 33);
+  auto diag_add = [&](int qh, const f32x16& dz) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) scr[(16 * (r >> 3) + 8 * g + (r & 7)) * 33 + l32] = dz[r];
+    const int e = lane - 31;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int t = 0; t < 32; ++t) {
+      const int qo = t + e;
+      acc += (qo >= 0 && qo < 32) ? scr[min(max(qo, 0), 31) * 33 + t] : 0.f;
+    }
+    const int d = qh - kw0 + e;
+    if (d >= 0 && d < ndist && acc != 0.f) atomicAdd(&dist_s[d], acc);
+  };
   // register r of half hf holds query q0 + 32 hf + 16 (r / 8) + 8 g + r % 8 against this lane's key.
   // Wave-uniform cases, each a straight loop: every pair visible in one
   // bucket (one wave sum) or in at most four (one wave sum per bucket, split
-  // at the bucket edges), every pair visible (per-distance adds), or masked
-  // (a masked pair adds 0 to its lane's spare slot, so masked lanes do not
-  // pile onto one address).
+  // at the bucket edges), every pair visible (sums per distance), or masked
+  // (masked pairs count zero, then sums per distance).
   auto elementwise = [&](int q0, int hf, f32x16& sacc, f32x16& pacc, const float* bias) {
     const int qh = q0 + 32 * hf;
     const int dmin = qh - (kw0 + 31), dmax = qh + 31 - kw0;
@@ -511,8 +534,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         pair(r, p, dz);
         sacc[r] = p;
         pacc[r] = dz;
-        atomicAdd(&dist_s[sb + 16 * (r >> 3) + 8 * g + (r & 7)], dz);
       }
+      diag_add(qh, pacc);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -522,8 +545,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         const bool vis = (i < L) & (key < L) & ((key == i) | ((key < i) & (key < hist)));
         sacc[r] = vis ? p : 0.f;
         pacc[r] = vis ? dz : 0.f;
-        atomicAdd(&dist_s[vis ? i - key : ndist + lane], vis ? dz : 0.f);
       }
+      diag_add(qh, pacc);
     }
   };
   // dV += P^T dO, dK += dZ^T Q over the half's 32 queries
