@@ -746,7 +746,7 @@ struct BwdWs {
   size_t dg, dout, g, da, dxh, xhat, zeros, part, drab_part, kv_items, q_items, total;
   int32_t n_kv, n_q, splits1, splits2;
 };
-constexpr int kBwdKeys = 128;  // keys per key-block item
+constexpr int kBwdKeys = kBwdKeyBlock;
 constexpr int kWgradTile = 128;
 
 int32_t wgrad_splits(int32_t M, int32_t N1, int32_t N2) {
@@ -803,9 +803,6 @@ hstu_status bwd_check(const hstu_layer_bwd_args* a, const char* who) {
   if (a->num_buckets <= 0 || a->num_buckets > 256)
     return fail(HSTU_ERR_INVALID, std::string(who) + ": num_buckets must be in [1, 256]");
   if (!(a->eps >= 0.f)) return fail(HSTU_ERR_INVALID, std::string(who) + ": eps must be >= 0");
-  for (const auto& us : p->users)
-    if (us.kv_len > 16384)
-      return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": sequences longer than 16384 are not supported");
   return HSTU_OK;
 }
 }  // namespace
@@ -888,8 +885,6 @@ hstu_status hstu_layer_backward(const hstu_layer_bwd_args* a, hipStream_t stream
     b.n_kv_items = static_cast<int32_t>(kv.size());
     b.q_items = reinterpret_cast<const BwdQItem*>(ws + w.q_items);
     b.n_q_items = static_cast<int32_t>(qi.size());
-    b.max_len = 0;
-    for (const auto& us : p->users) b.max_len = std::max(b.max_len, us.kv_len);
     if ((st = check_hip(timed(TK_BWD_ATTENTION, stream, [&] {
                           hipError_t e = launch_attn_bwd(b, stream);
                           return e != hipSuccess ? e : launch_drab_sum(drab_part, b.n_kv_items, a->num_buckets, a->drab, stream);

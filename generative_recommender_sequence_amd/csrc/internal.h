@@ -264,6 +264,7 @@ struct HeadArgs {
 hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s);
 
 // ---- backward (training; contiguous keys, every position computed) ----
+constexpr int kBwdKeyBlock = 64;  // keys per key-block item of the backward attention
 struct BwdKVItem {
   int32_t user, head, k0, pad;  // 128 keys from position k0
 };
@@ -282,7 +283,6 @@ struct BwdLaunch {
   int32_t n_kv_items;
   const BwdQItem* q_items;
   int32_t n_q_items;
-  int32_t max_len;        // longest user (sizes the per-distance sums)
 };
 hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s);
 hipError_t launch_drab_sum(const float* part, int32_t items, int32_t nb, float* drab, hipStream_t s);

@@ -6,7 +6,7 @@
 //
 //   gate_bwd_kernel   per row: dU = dg * LN(o), dLN(o) = dg * U through the
 //                     LayerNorm to do; also g = LN(o) * U for dW2
-//   attn_bwd_kv_kernel  per (user, head, 128 keys): dV and dK of those keys
+//   attn_bwd_kv_kernel  per (user, head, 64 keys): dV and dK of those keys
 //                     over every query that sees them, and the rab gradient
 //   attn_bwd_q_kernel   per (user, head, 128 queries): dQ over their keys
 //   silu_grad_kernel  ds = da * SiLU'(s) (s: the pre-activation of f1)
@@ -340,28 +340,33 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// attention, per 128-key block: dK, dV and the rab gradient
+// attention, per 64-key block: dK, dV and the rab gradient
 // ---------------------------------------------------------------------------
-// Each wave owns 32 keys; a step covers 64 queries as two 32-query halves
-// whose products are issued together, so one half's SiLU work overlaps the
-// other half's MFMAs.  The rab gradient is summed per distance i - j in LDS
-// (a wave gathers its 32 x 32 pairs by distance across lanes and adds one
-// atomic per distance; a wave whose pairs fall in at most four buckets adds
-// one wave sum per bucket), then folded into buckets, and written as this
-// item's partial.
-constexpr int KB = 128;        // keys per item (4 waves x 32)
-constexpr int QT = 64;         // queries per step
-constexpr int kTab = QT + KB;  // distances per step (191 used)
+// Two key groups of 32, each taken by two waves that split the head dims of
+// dK and dV between them (and both compute S and dP), so that a wave fits in
+// half the register file and two blocks share a CU; the block's K and V rows
+// sit in LDS.  A step covers 32 queries.  The rab gradient is summed per
+// distance i - j in LDS (one wave per key group gathers its 32 x 32 pairs by
+// distance across lanes and adds one atomic per distance; when its pairs
+// fall in at most four buckets it adds one wave sum per bucket), distances
+// past the LDS window (ragged tail steps) straight into their bucket; the
+// sums are folded into buckets and written as this item's partial.
+constexpr int KB = kBwdKeyBlock;  // keys per item: 2 groups of 32, each split over two waves by head dims
+constexpr int QT = 32;            // queries per step
+constexpr int kTab = QT + KB;     // distances per step (95 used)
+constexpr int kDistWin = 256;     // distances summed in LDS; larger ones (ragged tail steps) go to their bucket
 
-__global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
   __shared__ __attribute__((aligned(16))) uint16_t Q0s[QT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t D0s[QT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Q1s[QT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t D1s[QT * DH];
   __shared__ float bias0[kTab], bias1[kTab];
   __shared__ float drab_s[256];
-  __shared__ float diag_s[4 * 32 * 33];  // per-wave scratch of the distance sums
-  extern __shared__ float dist_s[];  // [max_len + 64]: sum of dz per distance (the last 64 unused)
+  __shared__ float diag_s[2 * 32 * 33];  // per-key-group scratch of the distance sums
+  __shared__ float dist_s[kDistWin];  // sum of dz per distance
+  __shared__ __attribute__((aligned(16))) uint16_t Kts[KB * DH];  // the block's keys: K and V rows
+  __shared__ __attribute__((aligned(16))) uint16_t Vts[KB * DH];
   lds_u16* const Q0 = (lds_u16*)Q0s;
   lds_u16* const D0 = (lds_u16*)D0s;
   lds_u16* const Q1 = (lds_u16*)Q1s;
@@ -377,26 +382,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   const int64_t ST = 4 * static_cast<int64_t>(inner);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = uniform(tid >> 6);
-  const int kw0 = k0 + 32 * wave;
+  const int kg = wave >> 1, hh = wave & 1;  // key group; half of the head dims this wave accumulates
+  const bool do_rab = hh == 0;              // one wave of each key group sums the rab gradient
+  const int kw0 = k0 + 32 * kg;
   const int key = kw0 + l32;
   const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur
   for (int i = tid; i < nb; i += 256) drab_s[i] = 0.f;
-  for (int i = tid; i < ndist + 64; i += 256) dist_s[i] = 0.f;
-  // this wave's keys as B operands (K for S = Q K^T, V for dP = dO V^T)
-  bf16x8 kf[DH / 16], vf[DH / 16];
-  {
-    const int kc = min(key, L - 1);
-    const uint16_t* kr = b.a + (row0 + kc) * ST + 3 * inner + h * DH;
-    const uint16_t* vr = b.a + (row0 + kc) * ST + 1 * inner + h * DH;
+  for (int i = tid; i < kDistWin; i += 256) dist_s[i] = 0.f;
+  lds_u16* const Kt = (lds_u16*)Kts;
+  lds_u16* const Vt = (lds_u16*)Vts;
+  const int lrow = lane >> 4, lslot = lane & 15;
+  // the block's K and V rows, staged once (wave w fills rows 16 w .. 16 w + 15);
+  // they are the B operands of S = Q K^T and dP = dO V^T
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * s + 8 * g));
-      vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vr + 16 * s + 8 * g));
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * i + lrow;
+    const int kc = min(k0 + r, L - 1);
+    const int ch = 8 * (lslot ^ swz(r));
+    const uint16_t* src = b.a + (row0 + kc) * ST + h * DH + ch;
+    dma16(src + 3 * inner, Kt + (16 * wave + 4 * i) * DH);
+    dma16(src + 1 * inner, Vt + (16 * wave + 4 * i) * DH);
   }
-  f32x16 dv_acc[DH / 32], dk_acc[DH / 32];
+  // dV and dK of this wave's 32 keys over head dims 64 hh .. 64 hh + 63
+  f32x16 dv_acc[2], dk_acc[2];
 #pragma unroll
-  for (int t = 0; t < DH / 32; ++t) dv_acc[t] = dk_acc[t] = f32x16{};
+  for (int t = 0; t < 2; ++t) dv_acc[t] = dk_acc[t] = f32x16{};
 
   // query steps that see some key of the block
   const int kb_end = min(k0 + KB, L);
@@ -405,16 +415,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
     if (k0 < qe && q0 < kb_end) return true;
     return k0 < hist && k0 < qe - 1;
   };
-  // copy: wave w fills rows 16 w .. 16 w + 15 of Q and dO, four rows per instruction
-  const int lrow = lane >> 4, lslot = lane & 15;
+  // copy: wave w fills rows 8 w .. 8 w + 7 of Q and dO, four rows per instruction
   auto copy_tile = [&](int q0, lds_u16* Qd, lds_u16* Dd) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wave + 4 * i + lrow;
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * wave + 4 * i + lrow;
       const int q = min(q0 + r, L - 1);
       const int ch = 8 * (lslot ^ swz(r));
-      dma16(b.a + (row0 + q) * ST + 2 * inner + h * DH + ch, Qd + (16 * wave + 4 * i) * DH);
-      dma16(b.dO + static_cast<int64_t>(row0 + q) * inner + h * DH + ch, Dd + (16 * wave + 4 * i) * DH);
+      dma16(b.a + (row0 + q) * ST + 2 * inner + h * DH + ch, Qd + (8 * wave + 4 * i) * DH);
+      dma16(b.dO + static_cast<int64_t>(row0 + q) * inner + h * DH + ch, Dd + (8 * wave + 4 * i) * DH);
     }
   };
   // distance table of a step: entry t is distance (q0 - k0 - (KB - 1)) + t
@@ -424,14 +433,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
       bias[tid] = d < 0 ? 0.f : b.rab[rel_bucket(d, nb)];
     }
   };
-  TrAddr tr;
-  tr.init(lane);
-  int qaddr[DH / 16];  // A operand of S: query row perm(l32) (+ 32 per half), chunk (2s + g)
+  // transposed-read addresses of this wave's two column blocks (2 hh, 2 hh + 1),
+  // selected once (a run-time index into the helper's table would go to scratch)
+  int tra[2][2];
   {
-    const int row = perm(l32);
+    TrAddr tr;
+    tr.init(lane);
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) qaddr[s] = row * DH + 8 * ((2 * s + g) ^ swz(row));
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) tra[r][t] = hh ? tr.a[r][2 + t] : tr.a[r][t];
   }
+  auto tr_read = [&](const lds_u16* T, int t, int ks) {
+    u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(T + tra[0][t] + 16 * ks * DH));
+    u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(T + tra[1][t] + 16 * ks * DH));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  // A operand of S: query row perm(l32); B operand: this lane's key row
+  // 32 kg + l32; chunk (2s + g) of each, swizzled (formed per use to save registers)
+  const int qrow = perm(l32), krow = 32 * kg + l32;
+  const int qbase = qrow * DH, qx = swz(qrow), kbase = krow * DH, kx = swz(krow);
 
   // Per-distance sums of a half's dz (register r of lane (l, g) holds key
   // offset l and query offset 16 (r / 8) + 8 g + r % 8, at distance D + that
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
   // slow on this chip: one per pair cost more than the rest of the step.
   // The scratch is private to the wave and a wave's LDS operations complete
   // in order, so no barrier is needed between the writes and the reads.
-  float* const scr = diag_s + wave * (32 * 33);
+  float* const scr = diag_s + kg * (32 * 33);
   auto diag_add = [&](int qh, const f32x16& dz) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) scr[(16 * (r >> 3) + 8 * g + (r & 7)) * 33 + l32] = dz[r];
@@ -453,20 +474,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
       acc += (qo >= 0 && qo < 32) ? scr[min(max(qo, 0), 31) * 33 + t] : 0.f;
     }
     const int d = qh - kw0 + e;
-    if (d >= 0 && d < ndist && acc != 0.f) atomicAdd(&dist_s[d], acc);
+    if (d >= 0 && d < ndist && acc != 0.f) {
+      if (d < kDistWin) atomicAdd(&dist_s[d], acc);
+      else atomicAdd(&drab_s[rel_bucket(d, nb)], acc);
+    }
   };
-  // register r of half hf holds query q0 + 32 hf + 16 (r / 8) + 8 g + r % 8 against this lane's key.
+  // register r holds query q0 + 16 (r / 8) + 8 g + r % 8 against this lane's key.
   // Wave-uniform cases, each a straight loop: every pair visible in one
   // bucket (one wave sum) or in at most four (one wave sum per bucket, split
   // at the bucket edges), every pair visible (sums per distance), or masked
   // (masked pairs count zero, then sums per distance).
-  auto elementwise = [&](int q0, int hf, f32x16& sacc, f32x16& pacc, const float* bias) {
-    const int qh = q0 + 32 * hf;
+  auto elementwise = [&](int q0, f32x16& sacc, f32x16& pacc, const float* bias) {
+    const int qh = q0;
     const int dmin = qh - (kw0 + 31), dmax = qh + 31 - kw0;
     const bool full = kw0 + 31 < qh && kw0 + 31 < hist && qh + 32 <= L && kw0 + 31 < L;
     const bool uni = full && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
-    const int tb = 32 * hf + (KB - 1) - (key - k0);  // table entry of register 0
-    const int sb = qh - key;                          // distance of register 0
+    const int tb = (KB - 1) - (key - k0);  // table entry of register 0
+    const int sb = qh - key;               // distance of register 0
     auto pair = [&](int r, float& p, float& dz) {
       const float z = sacc[r] + bias[tb + 16 * (r >> 3) + 8 * g + (r & 7)];
       const float sg = sigmoid(z);
@@ -487,8 +511,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         pacc[r] = dz;
         dsum += dz;
       }
-      dsum = wave_sum(dsum);
-      if (lane == 0) atomicAdd(&drab_s[bhi], dsum);
+      if (do_rab) {
+        dsum = wave_sum(dsum);
+        if (lane == 0) atomicAdd(&drab_s[bhi], dsum);
+      }
+    } else if (few && !do_rab) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p, dz;
+        pair(r, p, dz);
+        sacc[r] = p;
+        pacc[r] = dz;
+      }
     } else if (few) {
       int t[3];
 #pragma unroll
@@ -535,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         sacc[r] = p;
         pacc[r] = dz;
       }
-      diag_add(qh, pacc);
+      if (do_rab) diag_add(qh, pacc);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -546,11 +580,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         sacc[r] = vis ? p : 0.f;
         pacc[r] = vis ? dz : 0.f;
       }
-      diag_add(qh, pacc);
+      if (do_rab) diag_add(qh, pacc);
     }
   };
-  // dV += P^T dO, dK += dZ^T Q over the half's 32 queries
-  auto accumulate = [&](int hf, const f32x16& sacc, const f32x16& pacc, const lds_u16* Qs, const lds_u16* Ds) {
+  // dV += P^T dO, dK += dZ^T Q over the step's 32 queries, for this wave's
+  // half of the head dims (column blocks 2 hh and 2 hh + 1)
+  auto accumulate = [&](const f32x16& sacc, const f32x16& pacc, const lds_u16* Qs, const lds_u16* Ds) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pa, za;
@@ -560,27 +595,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
         za[e] = static_cast<__bf16>(pacc[8 * ks + e]);
       }
 #pragma unroll
-      for (int nt = 0; nt < DH / 32; ++nt) {
-        dv_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr.read(Ds, nt, 2 * hf + ks), dv_acc[nt], 0, 0, 0);
-        dk_acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, tr.read(Qs, nt, 2 * hf + ks), dk_acc[nt], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_read(Ds, t, ks), dv_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, tr_read(Qs, t, ks), dk_acc[t], 0, 0, 0);
       }
     }
   };
+  // S and dP over all head dims (both waves of a key group compute them)
   auto step = [&](int q0, const lds_u16* Qs, const lds_u16* Ds, const float* bias) {
-    f32x16 sacc[2], pacc[2];
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) sacc[hf] = pacc[hf] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qs + qaddr[s] + 32 * hf * DH), kf[s], sacc[hf], 0, 0, 0);
-        pacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Ds + qaddr[s] + 32 * hf * DH), vf[s], pacc[hf], 0, 0, 0);
-      }
-    elementwise(q0, 0, sacc[0], pacc[0], bias);
-    accumulate(0, sacc[0], pacc[0], Qs, Ds);
-    elementwise(q0, 1, sacc[1], pacc[1], bias);
-    accumulate(1, sacc[1], pacc[1], Qs, Ds);
+    for (int s = 0; s < DH / 16; ++s) {
+      const int qa_s = qbase + 8 * ((2 * s + g) ^ qx), ka_s = kbase + 8 * ((2 * s + g) ^ kx);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qs + qa_s), lds_row8(Kt + ka_s), sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Ds + qa_s), lds_row8(Vt + ka_s), pacc, 0, 0, 0);
+    }
+    elementwise(q0, sacc, pacc, bias);
+    accumulate(sacc, pacc, Qs, Ds);
   };
 
   int q0 = (k0 / QT) * QT;
@@ -614,36 +645,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(BwdLaunch b) {
     q0 = qn;
   }
   __syncthreads();
-  // fold the per-distance sums into buckets: thread t takes a contiguous run
-  // of distances (buckets rise with distance) and adds each bucket's run once
-  {
-    const int per = (ndist + 255) / 256;
-    const int d0 = tid * per, d1 = min(ndist, d0 + per);
-    float run = 0.f;
-    int cur = -1;
-    for (int dd = d0; dd < d1; ++dd) {
-      const int bk = rel_bucket(dd, nb);
-      if (bk != cur) {
-        if (cur >= 0 && run != 0.f) atomicAdd(&drab_s[cur], run);
-        cur = bk;
-        run = 0.f;
-      }
-      run += dist_s[dd];
-    }
-    if (cur >= 0 && run != 0.f) atomicAdd(&drab_s[cur], run);
-  }
+  // fold the per-distance sums into buckets (one distance a thread)
+  static_assert(kDistWin == 256, "one distance per thread");
+  if (tid < ndist && dist_s[tid] != 0.f) atomicAdd(&drab_s[rel_bucket(tid, nb)], dist_s[tid]);
   __syncthreads();
   for (int i = tid; i < nb; i += 256) b.drab_partial[static_cast<int64_t>(blockIdx.x) * nb + i] = drab_s[i];
-  // rows (keys) 8 (r / 4) + 4 g + r % 4 of this wave's 32, column 32 nt + l32
+  // rows (keys) 8 (r / 4) + 4 g + r % 4 of this wave's 32, column 32 (2 hh + t) + l32
 #pragma unroll
-  for (int nt = 0; nt < DH / 32; ++nt)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kk < L) {
-        uint16_t* dst = b.da + (row0 + kk) * ST + h * DH + 32 * nt + l32;
-        dst[1 * inner] = f2bf(dv_acc[nt][r]);
-        dst[3 * inner] = f2bf(dk_acc[nt][r]);
+        uint16_t* dst = b.da + (row0 + kk) * ST + h * DH + 32 * (2 * hh + t) + l32;
+        dst[1 * inner] = f2bf(dv_acc[t][r]);
+        dst[3 * inner] = f2bf(dk_acc[t][r]);
       }
     }
 }
@@ -885,11 +901,8 @@ hipError_t launch_wgrad(const void* A, int64_t lda, const void* B, int64_t ldb, 
 }
 
 hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
-  // per-distance rab-gradient sums of the longest user in LDS
-  const size_t dist_bytes = static_cast<size_t>(b.max_len + 64) * sizeof(float);
-  if (dist_bytes > (16384 + 64) * sizeof(float)) return hipErrorInvalidValue;
   if (b.n_kv_items > 0)
-    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(b.n_kv_items)), dim3(256), dist_bytes, s, b);
+    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(b.n_kv_items)), dim3(256), 0, s, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (b.n_q_items > 0)
