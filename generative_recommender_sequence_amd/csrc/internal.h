@@ -266,7 +266,7 @@ hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s);
 // ---- backward (training; contiguous keys, every position computed) ----
 constexpr int kBwdKeyBlock = 64;  // keys per key-block item of the backward attention
 struct BwdKVItem {
-  int32_t user, head, k0, pad;  // 128 keys from position k0
+  int32_t user, head, k0, pad;  // kBwdKeyBlock keys from position k0
 };
 struct BwdQItem {
   int32_t qblock, head;

@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   };
 
   // epilogue inputs fetched up front so that their latency hides under the
-  // k loop: each lane's row records (f1) or residual values (f2), and the
-  // block's column sums (f1, into LDS)
+  // k loop: each lane's row statistics and pool slots (f1) or residual
+  // values (f2), and the block's column sums (f1, into LDS)
   __shared__ __attribute__((aligned(16))) float cs_lds[EPI == 0 ? BN : 4];
   __shared__ __attribute__((aligned(16))) float hb_lds[EPI == 2 ? BN : 4];
   __shared__ __attribute__((aligned(16))) float hw_lds[EPI == 2 ? BN : 4];
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   const int nk = K / GBK;
   copy_k(0, A0, B0);
   if (EPI == 0 && tid < BN / 4) *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = cs_val;
-  __syncthreads();  // k step 0 in buffer 0 (and the prefetched row records in)
+  __syncthreads();  // k step 0 in buffer 0 (and the prefetched row statistics in)
   // f1: each lane's row statistics
   float mu[MT], rstd[MT];
   if (EPI == 0) {
