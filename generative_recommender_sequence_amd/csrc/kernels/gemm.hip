@@ -562,7 +562,7 @@ static unsigned gemm_grid(int32_t M, int32_t N) {
 hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, const float* colsum, const void* w1t,
                           const F1Args& f, int32_t M, int32_t N, int32_t K, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  constexpr int BM = 128, BN = 128;
+  constexpr int BN = 128;
   // a 128-column tile is one head of one chunk
   if (N % BN != 0 || K % GBK != 0 || f.dh != BN || f.inner % BN != 0) return hipErrorInvalidValue;
   if (slots < 1 || slots > kMaxStatSlots || K % slots != 0) return hipErrorInvalidValue;
@@ -582,9 +582,16 @@ hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, co
   r.dh = f.dh;
   r.page_size = f.page_size;
   r.s_out = static_cast<uint16_t*>(f.s_out);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 0>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1t),
-                     static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
+  // 128-row tiles, or 64-row tiles when the 128-row ones would leave CUs
+  // without a second block (few new tokens: candidates over a cached history)
+  const auto* A = static_cast<const uint16_t*>(x);
+  const auto* B = static_cast<const uint16_t*>(w1t);
+  if ((M + 127) / 128 * (N / BN) < 512)
+    hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 0>), dim3(gemm_grid<64, BN>(M, N)), dim3(256), 0, s, A, B,
+                       static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, BN, 0>), dim3(gemm_grid<128, BN>(M, N)), dim3(256), 0, s, A, B,
+                       static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
   return hipGetLastError();
 }
 
