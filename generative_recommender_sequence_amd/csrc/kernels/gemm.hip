@@ -55,6 +55,13 @@ __device__ __forceinline__ void dma16(const uint16_t* src, lds_u16* dst) {
   __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
+// two floats to a pair of bf16 (round to nearest even) in one conversion
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v{lo, hi}), bf16x2v));
+}
+
 // 16-byte chunk slot of logical chunk c in row r of a 64-wide tile (rows are
 // 128 B, two per 64 banks): 16 consecutive rows read at one logical chunk hit
 // 16 distinct bank groups.
@@ -319,8 +326,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
           v[2] += bf2f(r2[1] & 0xFFFFu);
           v[3] += bf2f(r2[1] >> 16);
         }
-        const u32x2 packed = {uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16),
-                              uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
+        const u32x2 packed = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
         if (EPI == 1) {  // the stored values, for the row statistics
           acc[i][j][4 * q + 0] = bf2f(packed[0] & 0xFFFFu);
           acc[i][j][4 * q + 1] = bf2f(packed[0] >> 16);
@@ -328,8 +334,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
           acc[i][j][4 * q + 3] = bf2f(packed[1] >> 16);
         }
         if (EPI == 0 && route.s_out) {  // pre-activation tap (f1), stored directly
-          const u32x2 pre = {uint32_t(f2bf(z[0])) | (uint32_t(f2bf(z[1])) << 16),
-                             uint32_t(f2bf(z[2])) | (uint32_t(f2bf(z[3])) << 16)};
+          const u32x2 pre = {pack_bf16(z[0], z[1]), pack_bf16(z[2], z[3])};
           *reinterpret_cast<u32x2*>(route.s_out + static_cast<int64_t>(m) * N + n0 + nl) = pre;
         }
         *(lds_u32x2*)(srow + 8 * ((nl >> 3) ^ (rl & 15)) + 4 * g) = packed;
