@@ -534,7 +534,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   L.q_stride = a->q_row_stride;
   L.rab = a->rab;
   L.num_buckets = a->num_buckets;
-  L.partials = static_cast<float*>(a->workspace);
+  L.partials = a->workspace;
   if ((st = fill_keys(L, p, a->dtype, a->k, a->v, a->kv_row_stride, a->cache, a->layer,
                       a->d_page_table, "hstu_attn_fwd")) != HSTU_OK)
     return st;
@@ -621,7 +621,7 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
   auto* ws = static_cast<unsigned char*>(a->workspace);
   void* xhat = ws + w.xhat;
   auto* uvqk = static_cast<unsigned char*>(a->uvqk_out ? a->uvqk_out : ws + w.uvqk);
-  float* partials = reinterpret_cast<float*>(ws + w.partials);
+  void* partials = ws + w.partials;
   void* g = a->g_out ? a->g_out : ws + w.g;
   const size_t es = esize(a->dtype);
   const int32_t M = p->n_new;

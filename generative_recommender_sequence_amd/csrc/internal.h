@@ -179,13 +179,14 @@ struct AttnLaunch {
   const int32_t* page_table;
   const float* rab;
   int32_t num_buckets;
-  float* partials;  // [n_slots][kBlockQ][dh]
+  void* partials;  // [n_slots][kBlockQ][dh]: bf16 from the bf16 kernel, fp32 from the fp32 one
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
-// Sums each row's partial slots in key order, scales by o_scale / n_u; then
+// Sums each row's partial slots (dtype, as the attention kernel of that dtype
+// writes them) in key order in fp32, scales by o_scale / n_u; then
 // writes o (fp32) and/or g = LayerNorm(o) * U (dtype).
-hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials,
+hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const void* partials,
                               float o_scale, const void* u, int64_t u_stride, float eps,
                               float* o_out, void* g_out, hipStream_t s);
 // The bf16 attention's partial sums carry a factor log2(e); this removes it.

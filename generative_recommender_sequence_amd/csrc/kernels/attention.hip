@@ -11,8 +11,9 @@
 // Work item = (user, head, block of <= 128 queries, range of 64-key tiles),
 // scheduled on the host.  Without a softmax there is no running max or
 // rescale: each work item writes the plain sum over its keys into its own
-// fp32 partial tile, and the reduction adds the tiles of a row in key order,
-// so the result does not depend on scheduling.
+// partial tile (the bf16 kernel rounds it to bf16, halving the bytes the
+// reduction reads; fp32 keeps fp32), and the reduction adds the tiles of a
+// row in key order in fp32, so the result does not depend on scheduling.
 //
 // bf16 kernel (gfx950, 256 threads = 4 waves, 32 queries per wave):
 //   S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (keys are the M rows, queries
@@ -358,17 +359,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     t = tn;
   }
 
-  if (!wave_active) return;
-  // ---- partial tile [BQ][DH] fp32 (times log2 e): lane holds column 32 nt + l32,
-  // rows 8(r/4)+4g+r%4 ----
-  float* out = a.partials + static_cast<int64_t>(w.slot) * BQ * DH;
+  // ---- partial tile [BQ][DH], rounded to bf16 (times log2 e).  A lane holds
+  // column 32 nt + l32 of rows 8(r/4)+4g+r%4; the tile goes through LDS (the
+  // K/V buffers, free after the last barrier: rows 0-63 in K0, 64-127 in V0)
+  // so that whole 256-byte rows leave in 16-byte stores ----
+  auto stage_row = [&](int row) -> lds_u16* { return row < 64 ? K0 + row * DH : V0 + (row - 64) * DH; };
+  if (wave_active) {
 #pragma unroll
-  for (int nt = 0; nt < DH / 32; ++nt)
+    for (int nt = 0; nt < DH / 32; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int row = wq0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (row < w.count) out[row * DH + 32 * nt + l32] = oacc[nt][r];
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int row = wq0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        stage_row(row)[32 * nt + l32] = f2bf(oacc[nt][r]);
+      }
+  }
+  __syncthreads();
+  uint16_t* out = static_cast<uint16_t*>(a.partials) + static_cast<int64_t>(w.slot) * BQ * DH;
+  const int srow = lane >> 4, sch = lane & 15;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = wq0 + 4 * it + srow;
+    if (row < w.count)
+      *reinterpret_cast<u32x4*>(out + row * DH + 8 * sch) =
+          *(const __attribute__((address_space(3))) u32x4*)(stage_row(row) + 8 * sch);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnLaunch a) {
     }
   }
   if (!qv) return;
-  float* out = a.partials + (static_cast<int64_t>(w.slot) * BQ + tid) * D;
+  float* out = static_cast<float*>(a.partials) + (static_cast<int64_t>(w.slot) * BQ + tid) * D;
   for (int e = 0; e < D; ++e) out[e] = o[e];
 }
 

@@ -3,7 +3,8 @@
 // output projection):
 //   pre-norm       x^ = LayerNorm(x) over d_model (no affine)
 //   reduce + gate  o = (1/n_u) * sum of the row's partial attention tiles in
-//                  key order; g = LayerNorm(o over all heads) * U
+//                  key order (tiles stored in the layer's dtype, summed in
+//                  fp32); g = LayerNorm(o over all heads) * U
 // One wave64 per row; statistics are two-pass from registers (mean, then the
 // mean of squared deviations), reduced with cross-lane shuffles.
 #include "common.h"
@@ -65,9 +66,16 @@ __device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
                                        uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16)};
 }
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-template <typename T, int kChunks>  // inner <= 64 * 4 * kChunks
+// four partial values as raw bits, widened once the round's loads are issued
+__device__ __forceinline__ u32x2 load_raw4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ f32x4 load_raw4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 widen4(u32x2 r) {
+  return f32x4{bf2f(r[0] & 0xFFFFu), bf2f(r[0] >> 16), bf2f(r[1] & 0xFFFFu), bf2f(r[1] >> 16)};
+}
+__device__ __forceinline__ f32x4 widen4(f32x4 v) { return v; }
+template <typename T, int kChunks>  // inner <= 64 * 4 * kChunks; partials of type T
 __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
-    PlanDev plan, const float* __restrict__ partials, float o_scale, const T* __restrict__ u,
+    PlanDev plan, const T* __restrict__ partials, float o_scale, const T* __restrict__ u,
     int64_t u_stride, float eps, float* __restrict__ o_out, T* __restrict__ g_out) {
   const int lane = threadIdx.x & 63;
   const int qb = blockIdx.x / kGroups;
@@ -84,12 +92,13 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
   if (local >= blk.count) return;
   const int row = blk.row0 + local;
   const float inv_n = plan.users[blk.user].inv_n * o_scale;
-  // the gate's U, fetched while the partial tiles are summed
-  f32x4 uv[kChunks];
+  // the gate's U, fetched while the partial tiles are summed (raw bits,
+  // widened at use; lanes past the row re-read its last values)
+  decltype(load_raw4(u)) uraw[kChunks];
+  if (g_out) {
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
-    const int c = 4 * (lane + 64 * k);
-    uv[k] = (g_out && c < inner) ? load4(u + static_cast<int64_t>(row) * u_stride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kChunks; ++k)
+      uraw[k] = load_raw4(u + static_cast<int64_t>(row) * u_stride + min(4 * (lane + 64 * k), inner - 4));
   }
   f32x4 o[kChunks];
 #pragma unroll
@@ -98,19 +107,20 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (c < inner) {
       const int e = c % dh;
-      const float* p = partials + (static_cast<int64_t>(sr[k].first) * kBlockQ + local) * dh + e;
+      const T* p = partials + (static_cast<int64_t>(sr[k].first) * kBlockQ + local) * dh + e;
       const int64_t step = static_cast<int64_t>(kBlockQ) * dh;
-      for (int s = 0; s < sr[k].count; s += 4) {
-        const int left = sr[k].count - s;
+      const int last = sr[k].count - 1;
+      for (int s = 0; s <= last; s += 4) {
+        // four loads issued together; past the last slot they re-read it and count zero
+        const auto v0 = load_raw4(p + s * step);
+        const auto v1 = load_raw4(p + min(s + 1, last) * step);
+        const auto v2 = load_raw4(p + min(s + 2, last) * step);
+        const auto v3 = load_raw4(p + min(s + 3, last) * step);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(p + s * step);
-        const f32x4 v1 = left > 1 ? *reinterpret_cast<const f32x4*>(p + (s + 1) * step) : z;
-        const f32x4 v2 = left > 2 ? *reinterpret_cast<const f32x4*>(p + (s + 2) * step) : z;
-        const f32x4 v3 = left > 3 ? *reinterpret_cast<const f32x4*>(p + (s + 3) * step) : z;
-        acc += v0;
-        if (left > 1) acc += v1;
-        if (left > 2) acc += v2;
-        if (left > 3) acc += v3;
+        acc += widen4(v0);
+        acc += s + 1 <= last ? widen4(v1) : z;
+        acc += s + 2 <= last ? widen4(v2) : z;
+        acc += s + 3 <= last ? widen4(v3) : z;
       }
       acc *= inv_n;
     }
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
     int c = 4 * (lane + 64 * k);
-    if (c < inner) store4(gr + c, (o[k] - mean) * rstd * uv[k]);
+    if (c < inner) store4(gr + c, (o[k] - mean) * rstd * widen4(uraw[k]));
   }
 }
 
@@ -165,7 +175,7 @@ hipError_t launch_layer_norm(int dtype, const void* x, void* xhat, int32_t rows,
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* partials,
+hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const void* partials,
                               float o_scale, const void* u, int64_t u_stride, float eps,
                               float* o_out, void* g_out, hipStream_t s) {
   if (plan.n_new == 0) return hipSuccess;
@@ -174,22 +184,24 @@ hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const float* parti
   dim3 grid(static_cast<unsigned>(plan.n_qblocks) * kGroups), block(64 * kRowsPerBlock);
   const bool narrow = plan.H * plan.dh <= 64 * 4 * 2;  // the configurations' 512 values a row
   if (dtype == HSTU_BF16) {
+    auto* pp = static_cast<const uint16_t*>(partials);
     auto* uu = static_cast<const uint16_t*>(u);
     auto* gg = static_cast<uint16_t*>(g_out);
     if (narrow)
-      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, 2>), grid, block, 0, s, plan, partials, o_scale, uu, u_stride,
+      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, 2>), grid, block, 0, s, plan, pp, o_scale, uu, u_stride,
                          eps, o_out, gg);
     else
-      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, kMaxPerLane / 4>), grid, block, 0, s, plan, partials, o_scale,
+      hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, kMaxPerLane / 4>), grid, block, 0, s, plan, pp, o_scale,
                          uu, u_stride, eps, o_out, gg);
   } else {
+    auto* pp = static_cast<const float*>(partials);
     auto* uu = static_cast<const float*>(u);
     auto* gg = static_cast<float*>(g_out);
     if (narrow)
-      hipLaunchKernelGGL((reduce_gate_kernel<float, 2>), grid, block, 0, s, plan, partials, o_scale, uu, u_stride,
+      hipLaunchKernelGGL((reduce_gate_kernel<float, 2>), grid, block, 0, s, plan, pp, o_scale, uu, u_stride,
                          eps, o_out, gg);
     else
-      hipLaunchKernelGGL((reduce_gate_kernel<float, kMaxPerLane / 4>), grid, block, 0, s, plan, partials, o_scale, uu,
+      hipLaunchKernelGGL((reduce_gate_kernel<float, kMaxPerLane / 4>), grid, block, 0, s, plan, pp, o_scale, uu,
                          u_stride, eps, o_out, gg);
   }
   return hipGetLastError();
