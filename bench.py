@@ -80,7 +80,7 @@ def main(argv=None):
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}), flush=True)
         sys.exit(2)
 
     import torch

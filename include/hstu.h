@@ -62,7 +62,7 @@ typedef enum {
   HSTU_ERR_NO_SPACE = 2,     /* not enough free pages; nothing changed */
   HSTU_ERR_UNKNOWN_USER = 3, /* user not in the cache */
   HSTU_ERR_DEVICE = 4,       /* a HIP call or kernel launch failed */
-  HSTU_ERR_UNSUPPORTED = 5   /* valid, but a shape this build has no kernel for */
+  HSTU_ERR_UNSUPPORTED = 5   /* valid, but a shape the library has no kernel for */
 } hstu_status;
 
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
