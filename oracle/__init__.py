@@ -8,7 +8,7 @@ Pieces:
   hstu_oracle.c   one layer / the attention, in double (plain definition)
   kv_oracle.c     cache metadata (allocator, LRU, canonical dump)
   brute.py        an independent float64 brute force (dense padded masks)
-  this file       ctypes wrappers, a layer-stack driver, and the pool-byte
+  this file       ctypes wrappers, a layer-stack runner, and the pool-byte
                   placement model of the KV table layout
 
 Every function here is pinned to something other than itself; the pins and
