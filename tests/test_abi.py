@@ -49,6 +49,11 @@ def test_plan_validation():
     p = hstu.hstu_plan_create(2, 128, [0, 3], [5, 0], [0, 0], [0.0, 3.0])   # n unused without new tokens
     hstu.hstu_plan_destroy(p)
     assert _status(hstu.hstu_plan_create, 2, 128, [70000], [0], [0]) == HSTU_ERR_UNSUPPORTED
+    # the exact limit: 65,535 positions are accepted, 65,536 are not
+    assert _status(hstu.hstu_plan_create, 2, 128, [64], [65472], [64]) == HSTU_ERR_UNSUPPORTED
+    p = hstu.hstu_plan_create(2, 128, [64], [65471], [64])
+    assert hstu.hstu_plan_get_info(p).n_new_total == 64
+    hstu.hstu_plan_destroy(p)
     assert _status(hstu.hstu_plan_create, 2, 128, [100], [0], [0], None, 32, 3) == HSTU_ERR_INVALID
     p = hstu.hstu_plan_create(2, 128, [], [], [])
     assert hstu.hstu_plan_get_info(p).n_new_total == 0

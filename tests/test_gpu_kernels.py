@@ -195,3 +195,35 @@ def test_attention_page_placement_and_size_invariance():
         req.close()
     assert torch.equal(outs[0], outs[1])
     assert torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_attention_at_maximum_length(paged):
+    """One user at the longest sequence a plan accepts (65,535 positions: a
+    65,471-token history and 64 candidates), bf16: distances up to 65,534
+    fall in the last rab bucket, and the paged user spans 1,024 pages."""
+    new_len, cached_len, n_targets = [64], [65471], [64]
+    say(f"attention at maximum length paged={paged}")
+    rng = np.random.default_rng(17)
+    H, dh, dtype = 2, 128, HSTU_BF16
+    t = runtime.tdtype(dtype)
+    if paged:
+        q, k, v, rab, L, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, 64, new_len, cached_len,
+                                                                n_targets, 3)
+        norm_n = [float(x) for x in L]
+        req = runtime.prepare_attn(cache, users, new_len, n_targets, norm_n, max_pages, H, dh)
+        o = runtime.attention(req, torch.from_numpy(q).to("cuda", t), H * dh, torch.from_numpy(rab).cuda(), dtype,
+                              cache=cache)
+    else:
+        q, k, v, rab, L = _attn_case(rng, dtype, H, dh, new_len, cached_len, n_targets)
+        norm_n = [float(x) for x in L]
+        req = runtime.prepare_attn(None, [0], new_len, n_targets, norm_n, 0, H, dh, cached_len=cached_len)
+        qd, kd, vd = (torch.from_numpy(a).to("cuda", t) for a in (q, k, v))
+        o = runtime.attention(req, qd, H * dh, torch.from_numpy(rab).cuda(), dtype, kd, vd, H * dh)
+    torch.cuda.synchronize()
+    assert L == [65535]
+    ref = oracle.attention(q, k, v, new_len, cached_len, L, n_targets, norm_n, rab, H, dh)
+    err = rel(to64(o), ref)
+    say(f"  rel err {err:.2e}")
+    assert err < TOL[dtype]
+    req.close()
