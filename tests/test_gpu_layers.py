@@ -214,3 +214,35 @@ def test_row_statistics_need_narrow_bf16():
     with pytest.raises(RuntimeError, match="d_model <= 512"):
         hstu.hstu_stack_forward([a], runtime.stream_handle())
     req.close()
+
+
+def test_empty_request_is_a_no_op():
+    """A request whose users bring no new tokens: attention returns no rows,
+    and the stack returns an empty output and leaves the cache as it was."""
+    from generative_recommender_sequence_amd import hstu
+    say("empty request")
+    w = _small("hit", "bf16", hist=[200, 33], T=16, layers=2)
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    users = scn.request_inputs()[0]
+    before = hstu.kv_lookup(scn.cache.h, users).copy()
+    free_before = hstu.kv_free_pages(scn.cache.h)
+    req = runtime.prepare(scn.cache, users, [0, 0], [0, 0], [1.0, 1.0], scn.max_pages, scn.cfg.num_heads,
+                          scn.cfg.head_dim)
+    assert int(req.info.n_new_total) == 0
+    x = torch.empty((0, scn.cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    y = runtime.forward(scn.model, req, x, scn.cache)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, scn.cfg.d_model)
+    assert np.array_equal(hstu.kv_lookup(scn.cache.h, users), before)
+    assert hstu.kv_free_pages(scn.cache.h) == free_before
+    req.close()
+    # attention alone over a contiguous prefix, with no queries
+    H, dh = scn.cfg.num_heads, scn.cfg.head_dim
+    areq = runtime.prepare_attn(None, [0, 1], [0, 0], [0, 0], [1.0, 1.0], 0, H, dh, cached_len=[5, 0])
+    kv = torch.zeros((5, H * dh), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((0, H * dh), dtype=torch.bfloat16, device="cuda")
+    o = runtime.attention(areq, q, H * dh, scn.model.rab[0], hstu.HSTU_BF16, kv, kv, H * dh)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (0, H * dh)
+    areq.close()
