@@ -227,3 +227,44 @@ def test_attention_at_maximum_length(paged):
     say(f"  rel err {err:.2e}")
     assert err < TOL[dtype]
     req.close()
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("paged", [False, True])
+def test_attention_random_jagged_batches(seed, paged):
+    """Seeded random batches (1-6 users, up to 900 positions each, a random
+    cached/new split and candidate count), bf16: the plan's splitting of each
+    (q-block, head) into pieces and the key-order sum of their partial tiles
+    on shapes no fixed case picks."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 7))
+    L = rng.integers(1, 901, size=B)
+    new_len = [int(rng.integers(0, l + 1)) for l in L]
+    cached_len = [int(l) - t for l, t in zip(L, new_len)]
+    n_targets = [int(rng.integers(0, t + 1)) if t else 0 for t in new_len]
+    say(f"attention random seed={seed} paged={paged} L={list(map(int, L))} new={new_len} T={n_targets}")
+    H, dh, dtype = 2, 128, HSTU_BF16
+    t = runtime.tdtype(dtype)
+    if paged:
+        q, k, v, rab, Ls, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, 32, new_len, cached_len,
+                                                                 n_targets, seed)
+        norm_n = [float(x) for x in Ls]
+        req = runtime.prepare_attn(cache, users, new_len, n_targets, norm_n, max_pages, H, dh)
+        o = runtime.attention(req, torch.from_numpy(q).to("cuda", t), H * dh, torch.from_numpy(rab).cuda(), dtype,
+                              cache=cache)
+    else:
+        q, k, v, rab, Ls = _attn_case(rng, dtype, H, dh, new_len, cached_len, n_targets)
+        norm_n = [float(x) for x in Ls]
+        req = runtime.prepare_attn(None, list(range(B)), new_len, n_targets, norm_n, 0, H, dh,
+                                   cached_len=cached_len)
+        qd, kd, vd = (torch.from_numpy(a).to("cuda", t) for a in (q, k, v))
+        o = runtime.attention(req, qd, H * dh, torch.from_numpy(rab).cuda(), dtype, kd, vd, H * dh)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, new_len, cached_len, Ls, n_targets, norm_n, rab, H, dh)
+    if ref.size:
+        err = rel(to64(o), ref)
+        say(f"  rel err {err:.2e}")
+        assert err < TOL[dtype]
+    else:
+        assert o.numel() == 0
+    req.close()
