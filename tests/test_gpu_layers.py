@@ -246,3 +246,24 @@ def test_empty_request_is_a_no_op():
     torch.cuda.synchronize()
     assert tuple(o.shape) == (0, H * dh)
     areq.close()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_layers_random_hit_and_miss_bf16(seed):
+    """Seeded random batches through two cached layers: 1-5 users with random
+    history lengths, candidate counts and hit/miss flags, page size 32 or 64."""
+    rng = np.random.default_rng(2000 + seed)
+    B = int(rng.integers(1, 6))
+    hist = [int(h) for h in rng.integers(1, 700, size=B)]
+    T = int(rng.integers(1, 65))
+    hit = [bool(b) for b in rng.integers(0, 2, size=B)]
+    P = int(rng.choice([32, 64]))
+    say(f"random layers seed={seed} hist={hist} T={T} hit={hit} P={P}")
+    w = _small("hit", "bf16", hist=hist, T=T, P=P, hit=hit, seed=seed)
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    req, x = scn.make_request()
+    per = run_layers_with_taps(scn, req, x)
+    worst = check_layers(scn, req, per, list(range(B)), f"random-{seed}")
+    _assert_within(worst, TOL[scn.dtype])
+    req.close()
