@@ -82,6 +82,67 @@ StagingRing& staging() {
   return r;
 }
 
+
+// Dispatch order of attention pieces (visible tiles, item), appended to out.
+// Block b runs on XCD b % 8, and each XCD starts its next block as soon as
+// one of its slots frees, independently of the others, so the launch ends
+// when the most loaded XCD drains.  Pieces of one (user, head) read the same
+// K/V and go to one XCD where the balance allows, sharing its L2: groups are
+// taken largest first, each onto the least-loaded XCD, and a piece that
+// would lift that XCD above an equal share of all tiles goes to the
+// least-loaded XCD instead.  Each XCD then runs its pieces longest first
+// (ties keep the group order), so that its last slots free together; XCD
+// x's k-th piece sits at index 8k + x and short queues are padded with no-op
+// entries (slot -1), so out grows by a multiple of 8.
+void dispatch_order(const std::vector<std::pair<int32_t, WorkItem>>& pieces, int32_t B, int32_t H,
+                    std::vector<WorkItem>& out) {
+  std::vector<std::vector<std::pair<int32_t, WorkItem>>> groups;
+  std::vector<int64_t> gcost;
+  std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1);
+  int64_t all = 0;
+  for (const auto& pc : pieces) {
+    int32_t key = pc.second.user * H + pc.second.head;
+    if (gid[key] < 0) {
+      gid[key] = static_cast<int32_t>(groups.size());
+      groups.emplace_back();
+      gcost.push_back(0);
+    }
+    groups[gid[key]].push_back(pc);
+    gcost[gid[key]] += pc.first;
+    all += pc.first;
+  }
+  const int64_t share = (all + kXcds - 1) / kXcds;
+  std::vector<int32_t> gorder(groups.size());
+  std::iota(gorder.begin(), gorder.end(), 0);
+  std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+  // (visible tiles, arrival order, item) per XCD
+  std::vector<std::vector<std::tuple<int32_t, int32_t, WorkItem>>> q(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  int32_t seq = 0;
+  auto least = [&]() { return static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin()); };
+  for (int32_t gi : gorder) {
+    auto& grp = groups[gi];
+    std::stable_sort(grp.begin(), grp.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+    const int home = least();
+    for (const auto& pc : grp) {
+      const int x = load[home] + pc.first <= share ? home : least();
+      q[x].emplace_back(pc.first, seq++, pc.second);
+      load[x] += pc.first;
+    }
+  }
+  size_t depth = 0;
+  for (auto& qq : q) {
+    std::sort(qq.begin(), qq.end(), [](const auto& a, const auto& b) {
+      return std::get<0>(a) != std::get<0>(b) ? std::get<0>(a) > std::get<0>(b) : std::get<1>(a) < std::get<1>(b);
+    });
+    depth = std::max(depth, qq.size());
+  }
+  WorkItem pad{};
+  pad.slot = -1;
+  for (size_t k = 0; k < depth; ++k)
+    for (int x = 0; x < kXcds; ++x) out.push_back(k < q[x].size() ? std::get<2>(q[x][k]) : pad);
+}
+
 }  // namespace
 
 namespace {
@@ -252,15 +313,35 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
   p->qb_slots.resize(static_cast<size_t>(nqb) * H);
   std::vector<std::pair<int32_t, WorkItem>> pieces;  // (visible tiles, item)
   int32_t slot = 0;
+  // page-table entries a paged piece over tiles [tb, te) stages
+  const int64_t P = d->page_size;
+  auto span_pages = [&](int64_t tb, int64_t te) -> int64_t {
+    return P > 0 ? (te * kTileK + P - 1) / P - tb * kTileK / P : 0;
+  };
+  std::vector<std::pair<int32_t, int32_t>> cuts;  // [lo, hi) into the visible-tile list
   for (int32_t b = 0; b < nqb; ++b) {
     const auto& v = vis[b];
     int32_t nv = static_cast<int32_t>(v.size());
     int32_t np = std::max<int32_t>(1, static_cast<int32_t>((nv + piece_tiles - 1) / piece_tiles));
+    // equal shares of the visible tiles, each cut again wherever its page
+    // span would pass kMaxItemPages (one tile spans at most 5 pages, P >= 16)
+    cuts.clear();
+    for (int32_t k = 0; k < np; ++k) {
+      int32_t lo = static_cast<int32_t>(static_cast<int64_t>(nv) * k / np);
+      int32_t hi = static_cast<int32_t>(static_cast<int64_t>(nv) * (k + 1) / np);
+      int32_t start = lo;
+      for (int32_t i = lo + 1; i < hi; ++i)
+        if (span_pages(v[start], v[i] + 1) > kMaxItemPages) {
+          cuts.emplace_back(start, i);
+          start = i;
+        }
+      cuts.emplace_back(start, hi);
+    }
+    const int32_t npc = static_cast<int32_t>(cuts.size());
     for (int32_t h = 0; h < H; ++h) {
-      p->qb_slots[static_cast<size_t>(b) * H + h] = SlotRange{slot, np};
-      for (int32_t k = 0; k < np; ++k) {
-        int32_t lo = static_cast<int32_t>(static_cast<int64_t>(nv) * k / np);
-        int32_t hi = static_cast<int32_t>(static_cast<int64_t>(nv) * (k + 1) / np);
+      p->qb_slots[static_cast<size_t>(b) * H + h] = SlotRange{slot, npc};
+      for (const auto& cut : cuts) {
+        const int32_t lo = cut.first, hi = cut.second;
         const QBlock& qb = p->qblocks[b];
         const UserInfo& ui = p->users[qb.user];
         WorkItem w{};
@@ -281,64 +362,20 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     }
   }
   p->n_slots = slot;
-  // Dispatch order.  Block b runs on XCD b % 8, and each XCD starts its
-  // next block as soon as one of its slots frees, independently of the
-  // others, so the launch ends when the most loaded XCD drains.  Pieces of
-  // one (user, head) read the same K/V and go to one XCD where the balance
-  // allows, sharing its L2: groups are taken largest first, each onto the
-  // least-loaded XCD, and a piece that would lift that XCD above an equal
-  // share of all tiles goes to the least-loaded XCD instead.  Each XCD then
-  // runs its pieces longest first (ties keep the group order), so that its
-  // last slots free together; XCD x's k-th piece sits at index 8k + x and
-  // short queues are padded with no-op entries (slot -1).
+  dispatch_order(pieces, B, H, p->items);
+  // The same pieces again as two consecutive orders, those of users with a
+  // cached prefix first (few queries against a long prefix: the bandwidth
+  // regime) and then the others (the full-recompute regime), when a request
+  // has both: instrumented runs launch them as two grids to time each.
   {
-    std::vector<std::vector<std::pair<int32_t, WorkItem>>> groups;
-    std::vector<int64_t> gcost;
-    std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1);
-    int64_t all = 0;
-    for (const auto& pc : pieces) {
-      int32_t key = pc.second.user * H + pc.second.head;
-      if (gid[key] < 0) {
-        gid[key] = static_cast<int32_t>(groups.size());
-        groups.emplace_back();
-        gcost.push_back(0);
-      }
-      groups[gid[key]].push_back(pc);
-      gcost[gid[key]] += pc.first;
-      all += pc.first;
+    std::vector<std::pair<int32_t, WorkItem>> cached_pieces, prefill_pieces;
+    for (const auto& pc : pieces)
+      (p->users[pc.second.user].start > 0 ? cached_pieces : prefill_pieces).push_back(pc);
+    if (!cached_pieces.empty() && !prefill_pieces.empty()) {
+      dispatch_order(cached_pieces, B, H, p->items_split);
+      p->n_split_cached = static_cast<int32_t>(p->items_split.size());
+      dispatch_order(prefill_pieces, B, H, p->items_split);
     }
-    const int64_t share = (all + kXcds - 1) / kXcds;
-    std::vector<int32_t> gorder(groups.size());
-    std::iota(gorder.begin(), gorder.end(), 0);
-    std::stable_sort(gorder.begin(), gorder.end(),
-                     [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
-    // (visible tiles, arrival order, item) per XCD
-    std::vector<std::vector<std::tuple<int32_t, int32_t, WorkItem>>> q(kXcds);
-    std::vector<int64_t> load(kXcds, 0);
-    int32_t seq = 0;
-    auto least = [&]() { return static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin()); };
-    for (int32_t gi : gorder) {
-      auto& grp = groups[gi];
-      std::stable_sort(grp.begin(), grp.end(),
-                       [](const auto& a, const auto& b) { return a.first > b.first; });
-      const int home = least();
-      for (const auto& pc : grp) {
-        const int x = load[home] + pc.first <= share ? home : least();
-        q[x].emplace_back(pc.first, seq++, pc.second);
-        load[x] += pc.first;
-      }
-    }
-    size_t depth = 0;
-    for (auto& qq : q) {
-      std::sort(qq.begin(), qq.end(), [](const auto& a, const auto& b) {
-        return std::get<0>(a) != std::get<0>(b) ? std::get<0>(a) > std::get<0>(b) : std::get<1>(a) < std::get<1>(b);
-      });
-      depth = std::max(depth, qq.size());
-    }
-    WorkItem pad{};
-    pad.slot = -1;
-    for (size_t k = 0; k < depth; ++k)
-      for (int x = 0; x < kXcds; ++x) p->items.push_back(k < q[x].size() ? std::get<2>(q[x][k]) : pad);
   }
 
   // packed device image
@@ -350,6 +387,7 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     return o;
   };
   p->off_items = region(p->items.size() * sizeof(WorkItem));
+  p->off_items_split = region(p->items_split.size() * sizeof(WorkItem));
   p->off_qblocks = region(p->qblocks.size() * sizeof(QBlock));
   p->off_qb_slots = region(p->qb_slots.size() * sizeof(SlotRange));
   p->off_users = region(p->users.size() * sizeof(UserInfo));
@@ -361,6 +399,7 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     if (bytes) std::memcpy(blob.data() + o, src, bytes);
   };
   copy(p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  copy(p->off_items_split, p->items_split.data(), p->items_split.size() * sizeof(WorkItem));
   copy(p->off_qblocks, p->qblocks.data(), p->qblocks.size() * sizeof(QBlock));
   copy(p->off_qb_slots, p->qb_slots.data(), p->qb_slots.size() * sizeof(SlotRange));
   copy(p->off_users, p->users.data(), p->users.size() * sizeof(UserInfo));
@@ -388,6 +427,23 @@ hstu_status hstu_plan_get_info(const hstu_plan* p, hstu_plan_info* info) {
   return ok();
 }
 
+hstu_status hstu_plan_get_items(const hstu_plan* p, int32_t* out, int32_t cap, int32_t* n) {
+  if (!p || !n || cap < 0 || (cap > 0 && !out)) return fail(HSTU_ERR_INVALID, "hstu_plan_get_items: bad argument");
+  const int32_t total = static_cast<int32_t>(p->items.size());
+  for (int32_t i = 0; i < std::min(total, cap); ++i) {
+    const WorkItem& w = p->items[i];
+    int32_t* r = out + static_cast<int64_t>(i) * 6;
+    r[0] = w.user;
+    r[1] = w.head;
+    r[2] = w.qblock;
+    r[3] = w.tile_begin;
+    r[4] = w.tile_end;
+    r[5] = w.slot;
+  }
+  *n = total;
+  return ok();
+}
+
 hstu_status hstu_plan_upload(hstu_plan* p, void* d_meta, size_t bytes, hipStream_t stream) {
   if (!p || !d_meta) return fail(HSTU_ERR_INVALID, "hstu_plan_upload: null argument");
   if (bytes < p->host_blob.size()) return fail(HSTU_ERR_INVALID, "hstu_plan_upload: buffer too small");
@@ -399,6 +455,7 @@ hstu_status hstu_plan_upload(hstu_plan* p, void* d_meta, size_t bytes, hipStream
   p->d_meta = d_meta;
   PlanDev& dv = p->dev;
   dv.items = reinterpret_cast<const WorkItem*>(base + p->off_items);
+  p->d_items_split = reinterpret_cast<const WorkItem*>(base + p->off_items_split);
   dv.qblocks = reinterpret_cast<const QBlock*>(base + p->off_qblocks);
   dv.qb_slots = reinterpret_cast<const SlotRange*>(base + p->off_qb_slots);
   dv.users = reinterpret_cast<const UserInfo*>(base + p->off_users);
@@ -510,6 +567,23 @@ static hstu_status fill_keys(AttnLaunch& L, const hstu_plan* p, int dtype, const
   return HSTU_OK;
 }
 
+// The attention launch of a plan: one grid, or in split timing mode, when
+// the plan mixes users with and without a cached prefix, its two orders as
+// two grids timed apart (the same items, so the same results).
+static hipError_t run_attention(const hstu_plan* p, const AttnLaunch& L, hipStream_t s) {
+  if (timing_mode() == 2 && !p->items_split.empty()) {
+    AttnLaunch A = L;
+    A.plan.items = p->d_items_split;
+    A.plan.n_items = p->n_split_cached;
+    hipError_t e = timed(TK_ATTN_CACHED, s, [&] { return launch_attention(A, s); });
+    if (e != hipSuccess) return e;
+    A.plan.items = p->d_items_split + p->n_split_cached;
+    A.plan.n_items = static_cast<int32_t>(p->items_split.size()) - p->n_split_cached;
+    return timed(TK_ATTN_PREFILL, s, [&] { return launch_attention(A, s); });
+  }
+  return timed(TK_ATTENTION, s, [&] { return launch_attention(L, s); });
+}
+
 hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   if (!a) return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null args");
   hstu_status st = check_plan(a->plan, "hstu_attn_fwd");
@@ -538,7 +612,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   if ((st = fill_keys(L, p, a->dtype, a->k, a->v, a->kv_row_stride, a->cache, a->layer,
                       a->d_page_table, "hstu_attn_fwd")) != HSTU_OK)
     return st;
-  if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_attn_fwd: attention")) != HSTU_OK)
+  if ((st = check_hip(run_attention(p, L, stream), "hstu_attn_fwd: attention")) != HSTU_OK)
     return st;
   return check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, partial_scale(a->dtype), nullptr, 0, 0.f, a->out,
                                       nullptr, stream); }),
@@ -709,7 +783,7 @@ hstu_status hstu_layer_forward(const hstu_layer_args* a, hipStream_t stream) {
                         "hstu_layer_forward: append")) != HSTU_OK)
       return st;
   }
-  if ((st = check_hip(timed(TK_ATTENTION, stream, [&] { return launch_attention(L, stream); }), "hstu_layer_forward: attention")) != HSTU_OK)
+  if ((st = check_hip(run_attention(p, L, stream), "hstu_layer_forward: attention")) != HSTU_OK)
     return st;
   if ((st = check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, partials, partial_scale(a->dtype), uvqk, 4 * inner, a->eps,
                                          a->o_out, g, stream); }),

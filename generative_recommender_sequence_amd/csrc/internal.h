@@ -26,6 +26,12 @@ hstu_status staged_upload(void* dst, const void* src, size_t bytes, hipStream_t 
 constexpr int kBlockQ = 128;  // queries per attention work item (4 waves x 32)
 constexpr int kTileK = 64;    // keys per staged K/V tile
 constexpr int kMaxPos = 65535;
+// Page-table entries one paged work item may stage in LDS: the pages from
+// the one holding its first key tile to the one holding its last.  The plan
+// cuts every piece whose span would exceed it (a piece can skip a masked gap
+// between history and candidate tiles, so its span is not bounded by its
+// tile count alone).
+constexpr int kMaxItemPages = 2048;
 
 // One attention work item: a block of up to kBlockQ queries of one user and
 // head, over the key tiles [tile_begin, tile_end) of that user.  Its result
@@ -85,6 +91,10 @@ struct hstu_plan {
   std::vector<int32_t> new_len, cached_len, n_targets;
   std::vector<float> norm_n;
   std::vector<hstu::WorkItem> items;
+  // items again as two dispatch orders (users with a cached prefix, then the
+  // rest), when the request has both kinds; empty otherwise
+  std::vector<hstu::WorkItem> items_split;
+  int32_t n_split_cached = 0;
   std::vector<hstu::QBlock> qblocks;
   std::vector<hstu::SlotRange> qb_slots;
   std::vector<hstu::UserInfo> users;
@@ -93,9 +103,10 @@ struct hstu_plan {
   int32_t n_slots = 0, n_new = 0, max_len = 0;
   int64_t pairs = 0;
   std::vector<unsigned char> host_blob;  // packed image of the device metadata
-  size_t off_items = 0, off_qblocks = 0, off_qb_slots = 0, off_users = 0, off_row_pos = 0,
+  size_t off_items = 0, off_items_split = 0, off_qblocks = 0, off_qb_slots = 0, off_users = 0, off_row_pos = 0,
          off_new_offsets = 0, off_start_pos = 0;
   void* d_meta = nullptr;  // set by hstu_plan_upload
+  const hstu::WorkItem* d_items_split = nullptr;
   hstu::PlanDev dev{};
 };
 
@@ -123,7 +134,10 @@ namespace hstu {
 
 // ---- optional event timing of launches (hstu_timing_*) ---------------------
 enum TimedKernel { TK_LAYER_NORM, TK_F1, TK_APPEND, TK_ATTENTION, TK_REDUCE, TK_F2, TK_GATHER, TK_HEAD,
-                   TK_BWD_ATTENTION, TK_BWD_GEMM, TK_BWD_ROWS, TK_COUNT };
+                   TK_BWD_ATTENTION, TK_BWD_GEMM, TK_BWD_ROWS, TK_ATTN_CACHED, TK_ATTN_PREFILL, TK_COUNT };
+// 0: off; 1: every launch timed; 2: as 1, and an attention over users of
+// both regimes (with and without a cached prefix) runs as two timed grids
+int timing_mode();
 // Brackets one launch: records a start event now and an end event when the
 // returned guard's end() is called (both on stream s), if timing is enabled.
 struct TimedLaunch {
@@ -179,13 +193,12 @@ struct AttnLaunch {
   const int32_t* page_table;
   const float* rab;
   int32_t num_buckets;
-  void* partials;  // [n_slots][kBlockQ][dh]: bf16 from the bf16 kernel, fp32 from the fp32 one
+  void* partials;  // fp32 [n_slots][kBlockQ][dh]
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
-// Sums each row's partial slots (dtype, as the attention kernel of that dtype
-// writes them) in key order in fp32, scales by o_scale / n_u; then
-// writes o (fp32) and/or g = LayerNorm(o) * U (dtype).
+// Sums each row's fp32 partial slots in key order, scales by o_scale / n_u;
+// then writes o (fp32) and/or g = LayerNorm(o) * U (dtype).
 hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const void* partials,
                               float o_scale, const void* u, int64_t u_stride, float eps,
                               float* o_out, void* g_out, hipStream_t s);

@@ -73,9 +73,9 @@ __device__ __forceinline__ f32x4 widen4(u32x2 r) {
   return f32x4{bf2f(r[0] & 0xFFFFu), bf2f(r[0] >> 16), bf2f(r[1] & 0xFFFFu), bf2f(r[1] >> 16)};
 }
 __device__ __forceinline__ f32x4 widen4(f32x4 v) { return v; }
-template <typename T, int kChunks>  // inner <= 64 * 4 * kChunks; partials of type T
+template <typename T, int kChunks>  // inner <= 64 * 4 * kChunks; U and g of type T, fp32 partials
 __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
-    PlanDev plan, const T* __restrict__ partials, float o_scale, const T* __restrict__ u,
+    PlanDev plan, const float* __restrict__ partials, float o_scale, const T* __restrict__ u,
     int64_t u_stride, float eps, float* __restrict__ o_out, T* __restrict__ g_out) {
   const int lane = threadIdx.x & 63;
   const int qb = blockIdx.x / kGroups;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void reduce_gate_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (c < inner) {
       const int e = c % dh;
-      const T* p = partials + (static_cast<int64_t>(sr[k].first) * kBlockQ + local) * dh + e;
+      const float* p = partials + (static_cast<int64_t>(sr[k].first) * kBlockQ + local) * dh + e;
       const int64_t step = static_cast<int64_t>(kBlockQ) * dh;
       const int last = sr[k].count - 1;
       for (int s = 0; s <= last; s += 4) {
@@ -183,8 +183,8 @@ hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const void* partia
   if (plan.n_qblocks == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(plan.n_qblocks) * kGroups), block(64 * kRowsPerBlock);
   const bool narrow = plan.H * plan.dh <= 64 * 4 * 2;  // the configurations' 512 values a row
+  auto* pp = static_cast<const float*>(partials);
   if (dtype == HSTU_BF16) {
-    auto* pp = static_cast<const uint16_t*>(partials);
     auto* uu = static_cast<const uint16_t*>(u);
     auto* gg = static_cast<uint16_t*>(g_out);
     if (narrow)
@@ -194,7 +194,6 @@ hipError_t launch_reduce_gate(int dtype, const PlanDev& plan, const void* partia
       hipLaunchKernelGGL((reduce_gate_kernel<uint16_t, kMaxPerLane / 4>), grid, block, 0, s, plan, pp, o_scale,
                          uu, u_stride, eps, o_out, gg);
   } else {
-    auto* pp = static_cast<const float*>(partials);
     auto* uu = static_cast<const float*>(u);
     auto* gg = static_cast<float*>(g_out);
     if (narrow)

@@ -12,11 +12,13 @@ namespace {
 
 const char* kNames[TK_COUNT] = {"layer_norm", "f1_gemm",  "append", "attention",
                                 "reduce_gate", "f2_gemm", "gather", "head",
-                                "bwd_attention", "bwd_gemm", "bwd_rows"};
+                                "bwd_attention", "bwd_gemm", "bwd_rows", "attention_cached",
+                                "attention_prefill"};
 
 struct TimingState {
   std::mutex mu;
   bool enabled = false;
+  int mode = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> recs[TK_COUNT];
   std::vector<hipEvent_t> spare;
 
@@ -48,6 +50,12 @@ TimingState& state() {
 
 }  // namespace
 
+int timing_mode() {
+  TimingState& st = state();
+  std::lock_guard<std::mutex> lk(st.mu);
+  return st.mode;
+}
+
 TimedLaunch::TimedLaunch(TimedKernel k, hipStream_t s) : kernel(k), stream(s), start_ev(nullptr) {
   TimingState& st = state();
   std::lock_guard<std::mutex> lk(st.mu);
@@ -77,6 +85,7 @@ hstu_status hstu_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(st.mu);
   st.clear();
   st.enabled = enable != 0;
+  st.mode = enable == 2 ? 2 : (enable != 0 ? 1 : 0);
   // events made up front, so that recording them costs no creation on the launch path
   while (st.enabled && st.spare.size() < 4096) {
     hipEvent_t e = nullptr;

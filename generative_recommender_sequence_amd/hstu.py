@@ -106,6 +106,7 @@ SIGNATURES = {
     "hstu_plan_destroy": (c_i32, [c_vp]),
     "hstu_plan_get_info": (c_i32, [c_vp, ctypes.POINTER(hstu_plan_info)]),
     "hstu_plan_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
+    "hstu_plan_get_items": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
     "hstu_attn_fwd": (c_i32, [ctypes.POINTER(hstu_attn_args), c_vp]),
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
@@ -125,7 +126,7 @@ SIGNATURES = {
 }
 
 TIMED_KERNELS = ("layer_norm", "f1_gemm", "append", "attention", "reduce_gate", "f2_gemm", "gather", "head",
-                 "bwd_attention", "bwd_gemm", "bwd_rows")
+                 "bwd_attention", "bwd_gemm", "bwd_rows", "attention_cached", "attention_prefill")
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -399,6 +400,16 @@ def hstu_plan_get_info(h: int) -> hstu_plan_info:
     return info
 
 
+def hstu_plan_get_items(h: int) -> np.ndarray:
+    """The plan's attention work items in launch order: int32 [n][6] =
+    (user, head, q-block, first key tile, end key tile, slot; -1 = padding)."""
+    n = c_i32()
+    _check(lib().hstu_plan_get_items(h, None, 0, ctypes.byref(n)), "hstu_plan_get_items")
+    out = np.zeros((max(n.value, 1), 6), np.int32)
+    _check(lib().hstu_plan_get_items(h, _ptr(out, c_i32), n.value, ctypes.byref(n)), "hstu_plan_get_items")
+    return out[:n.value]
+
+
 def hstu_plan_upload(h: int, d_meta: int, nbytes: int, stream: int):
     _check(lib().hstu_plan_upload(h, d_meta, nbytes, stream), "hstu_plan_upload")
 
@@ -483,8 +494,11 @@ class Batcher:
         return n.value
 
 
-def hstu_timing_enable(enable: bool):
-    _check(lib().hstu_timing_enable(1 if enable else 0), "hstu_timing_enable")
+def hstu_timing_enable(enable, split_attention: bool = False):
+    """enable: time every launch; split_attention: also run an attention over
+    users with and without a cached prefix as two grids, timed apart."""
+    mode = (2 if split_attention else 1) if enable else 0
+    _check(lib().hstu_timing_enable(mode), "hstu_timing_enable")
 
 
 def hstu_timing_read(kernel: str):

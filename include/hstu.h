@@ -248,6 +248,14 @@ hstu_status hstu_plan_get_info(const hstu_plan *plan, hstu_plan_info *info);
  * for the life of the process); the plan then refers to d_meta, which must
  * outlive its use. */
 hstu_status hstu_plan_upload(hstu_plan *plan, void *d_meta, size_t bytes, hipStream_t stream);
+/* The attention work items of a plan in launch order (block b of the grid
+ * runs record b), for inspection by tests and measurement tools: each record
+ * is int32 [6] = user, head, q-block (index in batch order of the blocks of
+ * up to 128 new tokens of one user), first and end key tile (64-key tiles
+ * [begin, end) of the user's positions), partial slot; slot -1 marks a no-op
+ * padding block.  Copies min(n_work_items, cap) records to out (host int32
+ * [cap][6]; may be NULL when cap == 0) and sets *n = n_work_items. */
+hstu_status hstu_plan_get_items(const hstu_plan *plan, int32_t *out, int32_t cap, int32_t *n);
 
 /* ======================================================================== */
 /* Attention [GR]: o = (1/n) sum SiLU(q.k + rab) v over the mask             */
@@ -479,7 +487,13 @@ hstu_status hstu_batcher_pending(const hstu_batcher *batcher, int32_t *n);
  * by a pair of HIP events recorded on the stream it is launched on.  Kernel
  * names: "layer_norm", "f1_gemm", "append", "attention", "reduce_gate",
  * "f2_gemm", "gather", "head", "bwd_attention", "bwd_gemm" (the backward's
- * products), "bwd_rows" (its row and elementwise kernels).  Enabling or disabling clears the records. */
+ * products), "bwd_rows" (its row and elementwise kernels).  With enable == 2
+ * the attention of a request that mixes users with a cached prefix and users
+ * without one runs as two grids, recorded as "attention_cached" (the users
+ * with a prefix: few queries against many cached keys) and
+ * "attention_prefill" (the rest); other requests record "attention".  The
+ * results are the same either way.  Enabling or disabling clears the
+ * records. */
 hstu_status hstu_timing_enable(int32_t enable);
 /* Waits for the recorded events of `kernel` and returns the number of
  * launches and their summed duration in milliseconds; clears them.

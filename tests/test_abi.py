@@ -122,3 +122,67 @@ def test_candidate_row_list():
     got = runtime.candidate_row_list(new_len, n_targets)
     assert got.tolist() == [3, 4, 5, 6, 7] + list(range(8, 72)) + [72, 73]
     assert np.array_equal(got, oracle.candidate_rows(new_len, n_targets))
+
+
+def _qblocks(new_len, cached_len):
+    out = []
+    for u, (t, c) in enumerate(zip(new_len, cached_len)):
+        for r in range(0, t, 128):
+            out.append((u, c + r, min(128, t - r)))
+    return out
+
+
+def _visible_tiles(pos0, count, L, T):
+    """64-key tiles holding at least one key some query of the block sees
+    (history queries see j <= i; candidates see the history and themselves)."""
+    hist = L - T
+    tiles = set()
+    for i in range(pos0, pos0 + count):
+        if i < hist:
+            tiles.update(range(0, i // 64 + 1))
+        else:
+            tiles.update(range(0, (hist - 1) // 64 + 1) if hist > 0 else [])
+            tiles.add(i // 64)
+    return sorted(tiles)
+
+
+@pytest.mark.parametrize("case", [
+    # a short history and tens of thousands of candidates in 16-token pages:
+    # a candidate block sees two history tiles and its own diagonal tiles,
+    # thousands of positions apart
+    ([40000], [100], [40000], 16),
+    ([30000], [3000], [30000], 16),
+    ([40000, 64, 700], [100, 5000, 0], [40000, 64, 64], 16),
+    ([300, 64, 1, 130], [0, 900, 0, 5000], [64, 64, 0, 130], 32),
+])
+def test_plan_items_cover_visible_tiles_within_page_limit(case):
+    """Every (q-block, head) gets consecutive slots whose items cover its
+    visible key tiles exactly once, in key order; no paged item stages more
+    than 2048 page-table entries (the attention kernel's LDS slice)."""
+    new_len, cached_len, n_targets, P = case
+    H = 2
+    L = [t + c for t, c in zip(new_len, cached_len)]
+    max_pages = max(-(-l // P) for l in L)
+    p = hstu.hstu_plan_create(H, 128, new_len, cached_len, n_targets, None, P, max_pages)
+    items = hstu.hstu_plan_get_items(p)
+    info = hstu.hstu_plan_get_info(p)
+    hstu.hstu_plan_destroy(p)
+    assert len(items) == info.n_work_items and len(items) % 8 == 0
+    real = items[items[:, 5] >= 0]
+    assert sorted(real[:, 5].tolist()) == list(range(info.n_partial_slots))
+    qbs = _qblocks(new_len, cached_len)
+    for (u, hd, qb, tb, te, slot) in real:
+        span = -(-(te * 64) // P) - (tb * 64) // P
+        assert span <= 2048, (u, hd, qb, tb, te, span)
+        assert qbs[qb][0] == u
+    for qb, (u, pos0, count) in enumerate(qbs):
+        want = _visible_tiles(pos0, count, L[u], n_targets[u])
+        for hd in range(H):
+            mine = real[(real[:, 2] == qb) & (real[:, 1] == hd)]
+            mine = mine[np.argsort(mine[:, 5])]
+            assert np.all(np.diff(mine[:, 5]) == 1)          # consecutive slots
+            got = []
+            for (_, _, _, tb, te, _) in mine:
+                got += [t for t in want if tb <= t < te]
+                assert tb in want and te - 1 in want        # pieces start and end on visible tiles
+            assert got == want, (qb, hd)

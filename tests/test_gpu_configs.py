@@ -13,6 +13,7 @@ import torch
 import oracle
 from generative_recommender_sequence_amd import hstu, runtime
 from generative_recommender_sequence_amd.workloads import workload_for
+from generative_recommender_sequence_amd.hstu import HSTU_BF16
 from gpu_checks import TOL, check_layers, rel, run_layers_with_taps, say, to64
 
 pytestmark = pytest.mark.gpu
@@ -23,35 +24,41 @@ def _gpu():
     runtime.require_gpu()
 
 
-def _sample(w, k=2):
-    """indices of the shortest users (the oracle runs them in seconds) and,
-    when cached, at least one cached user"""
+def _groups(name, w):
+    """Users compared with the oracle, in groups sized so that each group's
+    oracle run takes tens of seconds: every user of C1-C4 (C4's cache hits
+    together, its misses in two length-balanced halves), and C5's four longest
+    users (clipped at 16,384 history positions: the most pieces per row and
+    the widest spread over XCDs) and its two shortest."""
+    B = w.cfg.batch
     L = w.hist_len + w.n_targets
-    order = list(np.argsort(L, kind="stable"))
-    pick = order[:k]
-    if w.cfg.cache == "mixed":
-        hits = [b for b in order if w.hit[b]][:1]
-        miss = [b for b in order if not w.hit[b]][:1]
-        pick = hits + miss
-    return sorted(int(b) for b in pick)
+    order = [int(b) for b in np.argsort(L, kind="stable")]
+    if name == "C1":
+        return [[0, 1]]
+    if name == "C2":
+        return [sorted(order[0::2]), sorted(order[1::2])]
+    if name == "C3":
+        return [list(range(B))]
+    if name == "C4":
+        hits = [b for b in order if w.hit[b]]
+        miss = [b for b in order if not w.hit[b]]
+        return [sorted(hits), sorted(miss[0::2]), sorted(miss[1::2])]
+    if name == "C5":
+        return [sorted(order[-2:]), sorted(order[-4:-2]), sorted(order[:2])]
+    raise ValueError(name)
 
 
-def _oracle_cache_ops(scn):
-    """Replays the scenario's host cache operations on the oracle allocator."""
-    w, cfg = scn.w, scn.cfg
-    ko = oracle.KVOracle(w.num_pages, cfg.page_size, w.page_perm)
-    cached_users = [(w.user_ids[b], int(w.hist_len[b])) for b in range(cfg.batch) if w.hit[b]]
-    cached_users += [(w.stale_ids[s], int(w.stale_hist_len[s])) for s in range(len(w.stale_ids))]
-    order = [cached_users[i] for i in w.prefill_order]
-    if order:
-        rc, _, _ = ko.alloc([u for u, _ in order], [n for _, n in order], scn.max_pages)
-        assert rc == 0
-    return ko
+N_GROUPS = {"C1": 1, "C2": 2, "C3": 1, "C4": 3, "C5": 3}
+_RUN = {}
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
-def test_config_parity(name):
-    say(f"config {name}")
+def _config_run(name):
+    """The config's request run once through the stack with per-layer taps
+    (kept for the config's other user groups)."""
+    if name in _RUN:
+        return _RUN[name]
+    _RUN.clear()
+    torch.cuda.empty_cache()
     w = workload_for(name, 0)
     scn = runtime.Scenario(w)
     scn.prefill()
@@ -72,12 +79,52 @@ def test_config_parity(name):
         if w.cfg.cache == "mixed":
             assert len(req.evicted) > 0, "the pool must force an eviction"
     per = run_layers_with_taps(scn, req, x)
-    sample = _sample(w) if name != "C1" else [0, 1]
-    worst = check_layers(scn, req, per, sample, name)
+    _RUN[name] = (w, scn, req, per)
+    return _RUN[name]
+
+
+def _oracle_cache_ops(scn):
+    """Replays the scenario's host cache operations on the oracle allocator."""
+    w, cfg = scn.w, scn.cfg
+    ko = oracle.KVOracle(w.num_pages, cfg.page_size, w.page_perm)
+    cached_users = [(w.user_ids[b], int(w.hist_len[b])) for b in range(cfg.batch) if w.hit[b]]
+    cached_users += [(w.stale_ids[s], int(w.stale_hist_len[s])) for s in range(len(w.stale_ids))]
+    order = [cached_users[i] for i in w.prefill_order]
+    if order:
+        rc, _, _ = ko.alloc([u for u, _ in order], [n for _, n in order], scn.max_pages)
+        assert rc == 0
+    return ko
+
+
+@pytest.mark.parametrize("name,group", [(n, g) for n in ("C1", "C2", "C3", "C4", "C5") for g in range(N_GROUPS[n])])
+def test_config_parity(name, group):
+    say(f"config {name} group {group}")
+    w, scn, req, per = _config_run(name)
+    sample = _groups(name, w)[group]
+    say(f"  users {sample}: history {[int(w.hist_len[b]) for b in sample]}"
+        + (f" hit {[bool(w.hit[b]) for b in sample]}" if scn.cache is not None else ""))
+    worst = check_layers(scn, req, per, sample, f"{name}/{group}")
+    say(f"  worst: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
     tol = TOL[scn.dtype]
     bad = {k: v for k, v in worst.items() if not v < tol}
     assert not bad, f"{name} over tolerance {tol}: {bad}"
-    req.close()
+    if group == N_GROUPS[name] - 1:
+        _RUN.clear()
+        req.close()
+
+
+def test_config_groups_cover_the_requested_users():
+    for name in N_GROUPS:
+        w = workload_for(name, 0)
+        g = _groups(name, w)
+        assert len(g) == N_GROUPS[name]
+        flat = [b for grp in g for b in grp]
+        assert len(flat) == len(set(flat))
+        if name != "C5":
+            assert sorted(flat) == list(range(w.cfg.batch))
+        else:
+            L = w.hist_len + w.n_targets
+            assert sorted(L[flat])[-4:] == sorted(L)[-4:] and min(L[flat]) == min(L)
 
 
 def test_c3_candidates_match_c2_full_recompute():
@@ -100,7 +147,7 @@ def test_c3_candidates_match_c2_full_recompute():
     err_y = rel(y3, cand)
     err_b = rel(y3 - xc, cand - xc)
     say(f"  Y rel {err_y:.2e}, branch rel {err_b:.2e}")
-    assert err_y < 2e-2
-    assert err_b < 5e-2
+    assert err_y < TOL[HSTU_BF16]
+    assert err_b < TOL[HSTU_BF16]
     r2.close()
     r3.close()

@@ -268,3 +268,57 @@ def test_attention_random_jagged_batches(seed, paged):
     else:
         assert o.numel() == 0
     req.close()
+
+
+@pytest.mark.parametrize("case", [([40000], [100], [40000]), ([30000], [3000], [30000])])
+def test_attention_candidates_far_past_a_short_history(case):
+    """16-token pages, a short cached history and tens of thousands of
+    candidates: a candidate block sees the history's first tiles and its own
+    diagonal tiles thousands of positions later, so the plan must cut its
+    pieces for each to stage at most 2048 page-table entries."""
+    new_len, cached_len, n_targets = case
+    say(f"attention far candidates new={new_len} cached={cached_len} P=16")
+    rng = np.random.default_rng(23)
+    H, dh, dtype, P = 2, 128, HSTU_BF16, 16
+    q, k, v, rab, L, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, P, new_len, cached_len,
+                                                            n_targets, 9)
+    norm_n = [float(x) for x in L]
+    req = runtime.prepare_attn(cache, users, new_len, n_targets, norm_n, max_pages, H, dh)
+    items = hstu.hstu_plan_get_items(req.plan)
+    real = items[items[:, 5] >= 0]
+    span = -(-(real[:, 4] * 64) // P) - (real[:, 3] * 64) // P
+    assert span.max() <= 2048
+    o = runtime.attention(req, torch.from_numpy(q).to("cuda", runtime.tdtype(dtype)), H * dh,
+                          torch.from_numpy(rab).cuda(), dtype, cache=cache)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, new_len, cached_len, L, n_targets, norm_n, rab, H, dh)
+    err = rel(to64(o), ref)
+    say(f"  rel err {err:.2e} (largest item span {int(span.max())} pages)")
+    assert err < TOL[dtype]
+    req.close()
+
+
+def test_attention_split_timing_launch_is_identical():
+    """The instrumented launch that runs users with a cached prefix and users
+    without one as two grids gives byte-identical output to the single grid,
+    and records both parts."""
+    new_len, cached_len, n_targets = [64, 700, 64, 300], [1500, 0, 900, 0], [64, 64, 64, 17]
+    say("attention split timing launch")
+    rng = np.random.default_rng(31)
+    H, dh, dtype = 2, 128, HSTU_BF16
+    q, k, v, rab, L, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, 32, new_len, cached_len,
+                                                            n_targets, 4)
+    req = runtime.prepare_attn(cache, users, new_len, n_targets, None, max_pages, H, dh)
+    qd = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    rabd = torch.from_numpy(rab).cuda()
+    o1 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
+    hstu.hstu_timing_enable(True, split_attention=True)
+    o2 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
+    torch.cuda.synchronize()
+    n_c, _ = hstu.hstu_timing_read("attention_cached")
+    n_p, _ = hstu.hstu_timing_read("attention_prefill")
+    n_a, _ = hstu.hstu_timing_read("attention")
+    hstu.hstu_timing_enable(False)
+    assert (n_c, n_p, n_a) == (1, 1, 0)
+    assert torch.equal(o1, o2)
+    req.close()

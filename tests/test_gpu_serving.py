@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 T = 16
 CFG = Config("serve-small", "bf16", 4, 256, 2, 128, 2, ("lognormal", 150, 16, 300), T, "mixed", page_size=32)
 MAX_BATCH, USERS = 4, 24
-TOL_SERVE = 5e-2   # bf16 Y and K/V storage through two layers, then the head
+TOL_SERVE = 2e-2   # the per-layer bf16 bound, held through two layers and the head
 
 
 @pytest.fixture(scope="module", autouse=True)
