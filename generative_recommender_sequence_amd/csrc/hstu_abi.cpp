@@ -584,23 +584,27 @@ static hipError_t run_attention(const hstu_plan* p, const AttnLaunch& L, hipStre
   return timed(TK_ATTENTION, s, [&] { return launch_attention(L, s); });
 }
 
-hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
-  if (!a) return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null args");
-  hstu_status st = check_plan(a->plan, "hstu_attn_fwd");
+}  // extern "C"
+
+namespace hstu {
+hstu_status attn_fwd_into(const hstu_attn_args* a, void* partials, size_t partial_bytes, hipStream_t stream,
+                          const char* who) {
+  if (!a) return fail(HSTU_ERR_INVALID, std::string(who) + ": null args");
+  hstu_status st = check_plan(a->plan, who);
   if (st != HSTU_OK) return st;
   const hstu_plan* p = a->plan;
   const int H = p->desc.num_heads, dh = p->desc.head_dim;
-  if ((st = check_dtype_shape(a->dtype, dh, "hstu_attn_fwd")) != HSTU_OK) return st;
+  if ((st = check_dtype_shape(a->dtype, dh, who)) != HSTU_OK) return st;
   if (p->n_new == 0) return ok();
   if (!a->q || !a->out || !a->rab || a->num_buckets <= 0)
-    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: null q/out/rab or no buckets");
-  if (a->num_buckets > 256) return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_fwd: more than 256 buckets");
+    return fail(HSTU_ERR_INVALID, std::string(who) + ": null q/out/rab or no buckets");
+  if (a->num_buckets > 256) return fail(HSTU_ERR_UNSUPPORTED, std::string(who) + ": more than 256 buckets");
   if (a->q_row_stride < static_cast<int64_t>(H) * dh || a->q_row_stride % 8)
-    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: bad q_row_stride");
+    return fail(HSTU_ERR_INVALID, std::string(who) + ": bad q_row_stride");
   hstu_plan_info info{};
   hstu_plan_get_info(p, &info);
-  if (!a->workspace || a->workspace_bytes < info.attn_workspace_bytes)
-    return fail(HSTU_ERR_INVALID, "hstu_attn_fwd: workspace too small");
+  if (!partials || partial_bytes < info.attn_workspace_bytes)
+    return fail(HSTU_ERR_INVALID, std::string(who) + ": workspace too small");
   AttnLaunch L{};
   L.dtype = a->dtype;
   L.plan = p->dev;
@@ -608,15 +612,23 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   L.q_stride = a->q_row_stride;
   L.rab = a->rab;
   L.num_buckets = a->num_buckets;
-  L.partials = a->workspace;
+  L.partials = partials;
   if ((st = fill_keys(L, p, a->dtype, a->k, a->v, a->kv_row_stride, a->cache, a->layer,
-                      a->d_page_table, "hstu_attn_fwd")) != HSTU_OK)
+                      a->d_page_table, who)) != HSTU_OK)
     return st;
-  if ((st = check_hip(run_attention(p, L, stream), "hstu_attn_fwd: attention")) != HSTU_OK)
-    return st;
-  return check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, partial_scale(a->dtype), nullptr, 0, 0.f, a->out,
+  if ((st = check_hip(run_attention(p, L, stream), "attention")) != HSTU_OK) return fail(st, std::string(who) + ": " + g_last_error);
+  if ((st = check_hip(timed(TK_REDUCE, stream, [&] { return launch_reduce_gate(a->dtype, p->dev, L.partials, partial_scale(a->dtype), nullptr, 0, 0.f, a->out,
                                       nullptr, stream); }),
-                   "hstu_attn_fwd: reduce");
+                      "reduce")) != HSTU_OK)
+    return fail(st, std::string(who) + ": " + g_last_error);
+  return ok();
+}
+}  // namespace hstu
+
+extern "C" {
+
+hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
+  return attn_fwd_into(a, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, stream, "hstu_attn_fwd");
 }
 
 namespace {

@@ -196,6 +196,10 @@ struct AttnLaunch {
   void* partials;  // fp32 [n_slots][kBlockQ][dh]
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+// hstu_attn_fwd with its fp32 partial tiles in `partials` (partial_bytes
+// long); errors name `who`
+hstu_status attn_fwd_into(const hstu_attn_args* a, void* partials, size_t partial_bytes, hipStream_t stream,
+                          const char* who);
 
 // Sums each row's fp32 partial slots in key order, scales by o_scale / n_u;
 // then writes o (fp32) and/or g = LayerNorm(o) * U (dtype).

@@ -108,6 +108,8 @@ SIGNATURES = {
     "hstu_plan_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
     "hstu_plan_get_items": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
     "hstu_attn_fwd": (c_i32, [ctypes.POINTER(hstu_attn_args), c_vp]),
+    "hstu_attn_fwd_static": (c_i32, [ctypes.POINTER(hstu_attn_args), c_vp]),
+    "hstu_attn_static_scratch_bytes": (c_size, []),
     "hstu_layer_workspace_size": (c_i32, [ctypes.POINTER(hstu_layer_args), ctypes.POINTER(c_size)]),
     "hstu_layer_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_vp]),
     "hstu_stack_forward": (c_i32, [ctypes.POINTER(hstu_layer_args), c_i32, c_vp]),
@@ -416,6 +418,14 @@ def hstu_plan_upload(h: int, d_meta: int, nbytes: int, stream: int):
 
 def hstu_attn_fwd(args: hstu_attn_args, stream: int):
     _check(lib().hstu_attn_fwd(ctypes.byref(args), stream), "hstu_attn_fwd")
+
+
+def hstu_attn_fwd_static(args: hstu_attn_args, stream: int):
+    _check(lib().hstu_attn_fwd_static(ctypes.byref(args), stream), "hstu_attn_fwd_static")
+
+
+def hstu_attn_static_scratch_bytes() -> int:
+    return int(lib().hstu_attn_static_scratch_bytes())
 
 
 def hstu_layer_workspace_size(args: hstu_layer_args) -> int:

@@ -417,12 +417,17 @@ def candidate_row_list(new_len, n_targets) -> np.ndarray:
 
 def attention(req: Request, q: torch.Tensor, q_row_stride: int, rab: torch.Tensor, dtype: int,
               k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, kv_row_stride: int = 0,
-              cache: Optional[PagedCache] = None, layer: int = 0, stream=None) -> torch.Tensor:
-    """hstu_attn_fwd: o [N_new, H*dh] fp32 (includes 1/n)."""
+              cache: Optional[PagedCache] = None, layer: int = 0, stream=None,
+              static_scratch: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_attn_fwd: o [N_new, H*dh] fp32 (includes 1/n).  static_scratch:
+    hstu_attn_fwd_static instead (partial tiles in the library's static
+    device array; no workspace)."""
     s = stream_handle(stream)
     H, dh = req.num_heads, req.head_dim
-    out = torch.empty((int(req.info.n_new_total), H * dh), dtype=torch.float32, device=q.device)
-    ws = torch.empty(max(int(req.info.attn_workspace_bytes), 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((int(req.info.n_new_total), H * dh), dtype=torch.float32, device=q.device)
+    ws = None if static_scratch else torch.empty(max(int(req.info.attn_workspace_bytes), 256), dtype=torch.uint8,
+                                                  device=q.device)
     a = hstu.hstu_attn_args()
     a.dtype = dtype
     a.plan = req.plan
@@ -437,9 +442,12 @@ def attention(req: Request, q: torch.Tensor, q_row_stride: int, rab: torch.Tenso
     a.rab = rab.data_ptr()
     a.num_buckets = rab.numel()
     a.out = out.data_ptr()
-    a.workspace = ws.data_ptr()
-    a.workspace_bytes = ws.numel()
-    hstu.hstu_attn_fwd(a, s)
+    if static_scratch:
+        hstu.hstu_attn_fwd_static(a, s)
+    else:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+        hstu.hstu_attn_fwd(a, s)
     return out
 
 

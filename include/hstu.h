@@ -287,6 +287,22 @@ typedef struct {
 
 hstu_status hstu_attn_fwd(const hstu_attn_args *args, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation): hstu_attn_fwd
+ * with its fp32 partial tiles in a static device array the library owns, so
+ * args->workspace and workspace_bytes are ignored.  Same kernels and the same
+ * results as hstu_attn_fwd.  The array holds hstu_attn_static_scratch_bytes()
+ * bytes (128 MiB: 2048 partial tiles at head_dim 128); a plan whose
+ * attn_workspace_bytes is larger gets HSTU_ERR_UNSUPPORTED with nothing
+ * launched.  Every GPU the library runs on keeps its own copy until the
+ * process ends; its address is looked up on the first call on that device
+ * (with the device current).  Calls on one device share the array: calls
+ * that overlap on one device (several streams or host threads) race on it
+ * and must be serialised by the caller.  No device or host memory is
+ * allocated by this call. */
+hstu_status hstu_attn_fwd_static(const hstu_attn_args *args, hipStream_t stream);
+size_t hstu_attn_static_scratch_bytes(void);
+
 /* ======================================================================== */
 /* One HSTU layer [GR]: pre-norm, f1 + SiLU, (append), attention,            */
 /* LayerNorm(o) * U, f2 + residual                                           */
