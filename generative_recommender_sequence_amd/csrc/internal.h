@@ -315,4 +315,9 @@ hipError_t launch_fill_zero(void* p, int32_t n, hipStream_t s);
 hipError_t launch_wgrad(const void* A, int64_t lda, const void* B, int64_t ldb, int32_t M, int32_t N1, int32_t N2,
                         int32_t splits, const void* zeros, float* part, float* out, hipStream_t s);
 
+// ---- achievable-ceiling kernels (kernels/ceiling.hip) ----
+hipError_t launch_ceiling_mfma(int32_t blocks, int32_t iters, float* out, hipStream_t s);
+hipError_t launch_ceiling_read(const void* src, int64_t bytes, void* out, hipStream_t s);
+hipError_t launch_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 }  // namespace hstu

@@ -95,6 +95,24 @@ hstu_status hstu_timing_enable(int32_t enable) {
   return ok();
 }
 
+hstu_status hstu_ceiling_mfma(int32_t blocks, int32_t iters, float* out, hipStream_t stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return fail(HSTU_ERR_INVALID, "hstu_ceiling_mfma: bad argument");
+  return check_hip(launch_ceiling_mfma(blocks, iters, out, stream), "hstu_ceiling_mfma");
+}
+
+hstu_status hstu_ceiling_read(const void* src, int64_t bytes, void* out, hipStream_t stream) {
+  if (!src || !out || bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(HSTU_ERR_INVALID, "hstu_ceiling_read: bad argument");
+  return check_hip(launch_ceiling_read(src, bytes, out, stream), "hstu_ceiling_read");
+}
+
+hstu_status hstu_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16 ||
+      reinterpret_cast<uintptr_t>(dst) % 16)
+    return fail(HSTU_ERR_INVALID, "hstu_ceiling_copy: bad argument");
+  return check_hip(launch_ceiling_copy(src, dst, bytes, stream), "hstu_ceiling_copy");
+}
+
 hstu_status hstu_timing_read(const char* kernel, int32_t* launches, double* total_ms) {
   if (!kernel || !launches || !total_ms) return fail(HSTU_ERR_INVALID, "hstu_timing_read: null argument");
   int k = -1;

@@ -124,6 +124,9 @@ SIGNATURES = {
     "hstu_batcher_next": (c_i32, [c_vp, c_i64, P_i64, c_i32, P_i32, P_i64]),
     "hstu_batcher_pending": (c_i32, [c_vp, P_i32]),
     "hstu_timing_enable": (c_i32, [c_i32]),
+    "hstu_ceiling_mfma": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
+    "hstu_ceiling_read": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
+    "hstu_ceiling_copy": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "hstu_timing_read": (c_i32, [ctypes.c_char_p, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
 
@@ -528,3 +531,15 @@ def header_symbols(header_path: Optional[str] = None) -> Sequence[str]:
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                                  text, flags=re.M)))
+
+
+def hstu_ceiling_mfma(blocks: int, iters: int, out: int, stream: int):
+    _check(lib().hstu_ceiling_mfma(blocks, iters, out, stream), "hstu_ceiling_mfma")
+
+
+def hstu_ceiling_read(src: int, nbytes: int, out: int, stream: int):
+    _check(lib().hstu_ceiling_read(src, nbytes, out, stream), "hstu_ceiling_read")
+
+
+def hstu_ceiling_copy(src: int, dst: int, nbytes: int, stream: int):
+    _check(lib().hstu_ceiling_copy(src, dst, nbytes, stream), "hstu_ceiling_copy")

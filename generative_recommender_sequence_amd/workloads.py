@@ -235,11 +235,17 @@ def generate(cfg, seed: int = 0, *, batch: Optional[int] = None,
                     prefill_order, layers, x, x_stale, num_pages, page_perm)
 
 
-def workload_for(name: str, seed: int = 0, **kw) -> Workload:
-    """Workload by name; a workload that shares another's data draws with its seed and config."""
+def workload_for(name: str, seed: int = 0, num_layers: Optional[int] = None, **kw) -> Workload:
+    """Workload by name; a workload that shares another's data draws with its
+    seed and config.  num_layers: the same workload with a deeper or shallower
+    stack (the layers are drawn before the inputs, so the inputs differ)."""
     cfg = CONFIGS[name]
+    if num_layers is not None:
+        cfg = dataclasses.replace(cfg, num_layers=num_layers)
     if cfg.seed_alias is not None:
         base = CONFIGS[cfg.seed_alias]
+        if num_layers is not None:
+            base = dataclasses.replace(base, num_layers=num_layers)
         w = generate(base, seed, **kw)
         hist, T = w.hist_len, w.n_targets
         cfg2 = cfg if kw.get("batch") is None else dataclasses.replace(cfg, batch=kw["batch"])

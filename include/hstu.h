@@ -516,6 +516,22 @@ hstu_status hstu_timing_enable(int32_t enable);
  * INVALID for an unknown name. */
 hstu_status hstu_timing_read(const char *kernel, int32_t *launches, double *total_ms);
 
+/* Achievable ceilings of the two resources the layer is bound by (the
+ * benchmark quotes roofline fractions against these beside the vendor
+ * peaks; the pages state their target as a fraction of the HBM / MFMA
+ * roofline).  Each enqueues one kernel on `stream`; time it with events.
+ *  hstu_ceiling_mfma: `blocks` blocks of 256 threads, each wave issuing
+ *    4 * iters back-to-back bf16 32x32x16 MFMAs (4 * iters * 32768 FLOPs a
+ *    wave); `out` (device fp32 [blocks]) is written only in a case that
+ *    does not occur, so the launch does no memory traffic.
+ *  hstu_ceiling_read: reads `bytes` (multiple of 16, 16-byte aligned) of
+ *    device memory once; `out` (device uint32 [4096]) as above.
+ *  hstu_ceiling_copy: copies `bytes` from src to dst (device, disjoint).
+ * INVALID for null pointers, non-positive sizes or misalignment. */
+hstu_status hstu_ceiling_mfma(int32_t blocks, int32_t iters, float *out, hipStream_t stream);
+hstu_status hstu_ceiling_read(const void *src, int64_t bytes, void *out, hipStream_t stream);
+hstu_status hstu_ceiling_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

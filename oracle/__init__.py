@@ -67,6 +67,8 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_layer_norm.restype = None
@@ -142,6 +144,11 @@ def offsets(lengths: Sequence[int]) -> np.ndarray:
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return load(0).oracle_threads()
+
+
+def set_threads(n: int):
+    """Threads of the oracle's parallel loops from now on (e.g. 1)."""
+    load(0).oracle_set_threads(int(n))
 
 
 def silu(z: float, mutant: int = 0) -> float:

@@ -54,6 +54,8 @@
 
 /* threads an OpenMP region of the oracle uses */
 int oracle_threads(void) { return omp_get_max_threads(); }
+/* sets that number (n >= 1), e.g. 1 for a single-threaded timing */
+void oracle_set_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
 
 /* ------------------------------------------------------------------------ */
 /* elementwise pieces                                                        */

@@ -48,10 +48,11 @@ def half_ulp(y: np.ndarray, dtype: int) -> np.ndarray:
     return 2.0 ** (e - mant)
 
 
-def branch_excess(y_gpu, y_ref, x, dtype) -> float:
-    """max(|(y_gpu - x) - (y_ref - x)| - half_ulp(y_ref)) / max|y_ref - x|"""
+def branch_excess(y_gpu, y_ref, x, dtype, ulps: int = 1) -> float:
+    """max(|(y_gpu - x) - (y_ref - x)| - ulps * half_ulp(y_ref)) / max|y_ref - x|
+    (ulps = 2 when y_ref is itself a rounded stored value)"""
     br = y_ref - x
-    err = np.abs(y_gpu - y_ref) - half_ulp(y_ref, dtype)
+    err = np.abs(y_gpu - y_ref) - ulps * half_ulp(y_ref, dtype)
     return float(max(np.max(err), 0.0) / max(np.max(np.abs(br)), 1e-30)) if br.size else 0.0
 
 

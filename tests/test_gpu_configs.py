@@ -14,7 +14,7 @@ import oracle
 from generative_recommender_sequence_amd import hstu, runtime
 from generative_recommender_sequence_amd.workloads import workload_for
 from generative_recommender_sequence_amd.hstu import HSTU_BF16
-from gpu_checks import TOL, check_layers, rel, run_layers_with_taps, say, to64
+from gpu_checks import TOL, branch_excess, check_layers, rel, run_layers_with_taps, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -145,8 +145,11 @@ def test_c3_candidates_match_c2_full_recompute():
     cand = np.concatenate([y2[off[b + 1] - T:off[b + 1]] for b in range(w3.cfg.batch)])
     xc = to64(x3)
     err_y = rel(y3, cand)
-    err_b = rel(y3 - xc, cand - xc)
-    say(f"  Y rel {err_y:.2e}, branch rel {err_b:.2e}")
+    # both sides store Y in bf16: their difference holds up to one unit in
+    # the last place of Y (half from each rounding) that is no error of the
+    # branch, and Y is several times the branch
+    err_b = branch_excess(y3, cand, xc, HSTU_BF16, ulps=2)
+    say(f"  Y rel {err_y:.2e}, branch rel {rel(y3 - xc, cand - xc):.2e}, branch beyond storage rounding {err_b:.2e}")
     assert err_y < TOL[HSTU_BF16]
     assert err_b < TOL[HSTU_BF16]
     r2.close()
