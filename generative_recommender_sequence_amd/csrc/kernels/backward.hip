@@ -362,9 +362,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
   __shared__ __attribute__((aligned(16))) uint16_t Q1s[QT * DH];
   __shared__ __attribute__((aligned(16))) uint16_t D1s[QT * DH];
   __shared__ float bias0[kTab], bias1[kTab];
-  __shared__ float drab_s[256];
+  // rab-gradient sums, private to each key group's summing wave (one writer
+  // each, adds in program order: the result does not depend on scheduling)
+  __shared__ float drab_s[2][256];      // per bucket
+  __shared__ float dist_s[2][kDistWin];  // per distance
+  __shared__ float far_s[2][64];         // a step's sums at distances past the window, per lane
   __shared__ float diag_s[2 * 32 * 33];  // per-key-group scratch of the distance sums
-  __shared__ float dist_s[kDistWin];  // sum of dz per distance
   __shared__ __attribute__((aligned(16))) uint16_t Kts[KB * DH];  // the block's keys: K and V rows
   __shared__ __attribute__((aligned(16))) uint16_t Vts[KB * DH];
   lds_u16* const Q0 = (lds_u16*)Q0s;
@@ -387,8 +390,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
   const int kw0 = k0 + 32 * kg;
   const int key = kw0 + l32;
   const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur
-  for (int i = tid; i < nb; i += 256) drab_s[i] = 0.f;
-  for (int i = tid; i < kDistWin; i += 256) dist_s[i] = 0.f;
+  for (int i = tid; i < 2 * 256; i += 256) drab_s[i >> 8][i & 255] = 0.f;
+  for (int i = tid; i < 2 * kDistWin; i += 256) dist_s[i / kDistWin][i % kDistWin] = 0.f;
   lds_u16* const Kt = (lds_u16*)Kts;
   lds_u16* const Vt = (lds_u16*)Vts;
   const int lrow = lane >> 4, lslot = lane & 15;
@@ -458,10 +461,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
   // offset l and query offset 16 (r / 8) + 8 g + r % 8, at distance D + that
   // offset - l, D = qh - kw0): the wave writes its 32 x 32 tile to its own
   // LDS scratch, each lane sums one diagonal (query offset - key offset =
-  // lane - 31) and adds it with a single LDS atomic.  Float LDS atomics are
-  // slow on this chip: one per pair cost more than the rest of the step.
-  // The scratch is private to the wave and a wave's LDS operations complete
-  // in order, so no barrier is needed between the writes and the reads.
+  // lane - 31) and adds it to its distance's sum (the lanes' distances are
+  // distinct, so one plain add each).  Distances past the window (ragged
+  // tail steps) go to their buckets one lane after another.  Float LDS
+  // atomics are slow on this chip (one per pair cost more than the rest of
+  // the step) and would make the sums depend on scheduling.  The scratch is
+  // private to the wave and a wave's LDS operations complete in order, so no
+  // barrier is needed between the writes and the reads.
   float* const scr = diag_s + kg * (32 * 33);
   auto diag_add = [&](int qh, const f32x16& dz) {
 #pragma unroll
@@ -474,9 +480,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       acc += (qo >= 0 && qo < 32) ? scr[min(max(qo, 0), 31) * 33 + t] : 0.f;
     }
     const int d = qh - kw0 + e;
-    if (d >= 0 && d < ndist && acc != 0.f) {
-      if (d < kDistWin) atomicAdd(&dist_s[d], acc);
-      else atomicAdd(&drab_s[rel_bucket(d, nb)], acc);
+    const bool in = d >= 0 && d < ndist;
+    if (in && d < kDistWin) dist_s[kg][d] += acc;
+    if (__any(in && d >= kDistWin)) {
+      far_s[kg][lane] = in && d >= kDistWin ? acc : 0.f;
+      if (lane == 0) {
+        for (int l = 0; l < 64; ++l) {
+          const int dl = qh - kw0 + l - 31;
+          if (dl >= kDistWin && dl < ndist) drab_s[kg][rel_bucket(dl, nb)] += far_s[kg][l];
+        }
+      }
     }
   };
   // register r holds query q0 + 16 (r / 8) + 8 g + r % 8 against this lane's key.
@@ -513,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       }
       if (do_rab) {
         dsum = wave_sum(dsum);
-        if (lane == 0) atomicAdd(&drab_s[bhi], dsum);
+        if (lane == 0) drab_s[kg][bhi] += dsum;
       }
     } else if (few && !do_rab) {
 #pragma unroll
@@ -556,10 +569,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       s2 = wave_sum(s2);
       s3 = wave_sum(s3);
       if (lane == 0) {
-        atomicAdd(&drab_s[blo], s_all - s1);
-        if (blo + 1 <= bhi) atomicAdd(&drab_s[blo + 1], s1 - s2);
-        if (blo + 2 <= bhi) atomicAdd(&drab_s[blo + 2], s2 - s3);
-        if (blo + 3 <= bhi) atomicAdd(&drab_s[blo + 3], s3);
+        drab_s[kg][blo] += s_all - s1;
+        if (blo + 1 <= bhi) drab_s[kg][blo + 1] += s1 - s2;
+        if (blo + 2 <= bhi) drab_s[kg][blo + 2] += s2 - s3;
+        if (blo + 3 <= bhi) drab_s[kg][blo + 3] += s3;
       }
     } else if (full) {
 #pragma unroll
@@ -645,11 +658,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
     q0 = qn;
   }
   __syncthreads();
-  // fold the per-distance sums into buckets (one distance a thread)
-  static_assert(kDistWin == 256, "one distance per thread");
-  if (tid < ndist && dist_s[tid] != 0.f) atomicAdd(&drab_s[rel_bucket(tid, nb)], dist_s[tid]);
-  __syncthreads();
-  for (int i = tid; i < nb; i += 256) b.drab_partial[static_cast<int64_t>(blockIdx.x) * nb + i] = drab_s[i];
+  // this item's partial, one bucket a thread, in a fixed order: the two key
+  // groups' bucket sums, then their per-distance sums in increasing distance
+  // (buckets grow with distance, so bucket k's distances are one range,
+  // found by bisection)
+  const int dend = min(ndist, kDistWin);
+  auto first_at_least = [&](int kk) {  // first distance in [0, dend) of bucket >= kk, or dend
+    int lo = 0, hi = dend;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (rel_bucket(mid, nb) >= kk) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  for (int k = tid; k < nb; k += 256) {
+    float sum = drab_s[0][k] + drab_s[1][k];
+    const int d1 = first_at_least(k + 1);
+    for (int d = first_at_least(k); d < d1; ++d) sum += dist_s[0][d] + dist_s[1][d];
+    b.drab_partial[static_cast<int64_t>(blockIdx.x) * nb + k] = sum;
+  }
   // rows (keys) 8 (r / 4) + 4 g + r % 4 of this wave's 32, column 32 (2 hh + t) + l32
 #pragma unroll
   for (int t = 0; t < 2; ++t)

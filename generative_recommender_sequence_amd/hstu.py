@@ -14,7 +14,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libhstu.so")
+# HSTU_LIBRARY names another build of the same ABI (the tests' host-only
+# sanitizer build); by default the in-tree HIP library
+LIB_PATH = os.environ.get("HSTU_LIBRARY") or os.path.join(PKG, "libhstu.so")
 
 HSTU_OK, HSTU_ERR_INVALID, HSTU_ERR_NO_SPACE, HSTU_ERR_UNKNOWN_USER, HSTU_ERR_DEVICE, \
     HSTU_ERR_UNSUPPORTED = range(6)

@@ -204,7 +204,13 @@ hstu_status kv_page_append(const hstu_kv_cache *cache, int32_t layer, int32_t B,
                            const void *v_new, int64_t row_stride, int32_t n_new_total,
                            hipStream_t stream);
 
-/* gather: copies positions 0..d_kv_len[b]-1 of each user from the pages of
+/* gather [DT, KV cache section: the cached history is read back from the
+ * paged table instead of being recomputed]: the read side of
+ * kv_page_append, for callers that want a user's cached K/V as contiguous
+ * rows (inspection, export, a kernel without page-table addressing; the
+ * library's own attention reads the pages in place and does not use it).
+ * The pages name lookup, allocation, append and eviction, not a gather by
+ * name.  Copies positions 0..d_kv_len[b]-1 of each user from the pages of
  * `layer` to contiguous rows d_out_offsets[b].. of k_out / v_out (device,
  * [n_out_total][H*dh]).  Byte-exact copy. */
 hstu_status kv_page_gather(const hstu_kv_cache *cache, int32_t layer, int32_t B,
@@ -386,8 +392,9 @@ hstu_status hstu_stack_forward(const hstu_layer_args *layers, int32_t n, hipStre
  * c_u = 0).  bf16 only; head_dim 128, H*head_dim <= 512.  The forward pass
  * supplies what the backward reuses, through hstu_layer_forward's taps:
  * uvqk_out (SiLU'd [U|V|Q|K]), s_out (the pre-activation) and o_out.
- * Activation gradients are bf16, weight and bias gradients fp32.  drab is
- * summed with LDS float atomics, so its low bits may differ between runs. */
+ * Activation gradients are bf16, weight and bias gradients fp32.  Every sum
+ * runs in a fixed order (no float atomics), so repeated calls give
+ * bit-identical gradients. */
 typedef struct {
   hstu_dtype dtype;          /* HSTU_BF16 */
   int32_t d_model;           /* multiple of 128, <= 2048 */

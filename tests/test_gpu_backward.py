@@ -90,3 +90,27 @@ def test_two_layer_chain():
         bad = {k: v for k, v in errs.items() if not v < TOL_BWD}
         assert not bad, (li, bad)
     req.close()
+
+
+def test_backward_is_deterministic():
+    """Every gradient, drab included, is bit-identical across repeated runs
+    in one process: the rab gradient is summed per item in a fixed order and
+    the items' partials in item order (no float atomics); users longer than
+    the 256-distance window exercise the far-distance path too."""
+    say("backward determinism")
+    w = _case([700, 1000, 33], 64, seed=4)
+    scn = runtime.Scenario(w)
+    req, x = scn.make_request()
+    y, saved = runtime.forward_for_backward(scn.model, req, x)
+    dy = torch.from_numpy(round_bf16(np.random.default_rng(8).standard_normal(tuple(y.shape)).astype(
+        np.float32))).cuda().to(torch.bfloat16)
+    runs = []
+    for _ in range(3):
+        dx, grads = runtime.backward(scn.model, req, saved, dy)
+        torch.cuda.synchronize()
+        runs.append((dx.clone(), {k: v.clone() for k, v in grads[0].items()}))
+    for dx, g in runs[1:]:
+        assert torch.equal(dx, runs[0][0])
+        for k in ("dw1", "dw2", "drab"):
+            assert torch.equal(g[k], runs[0][1][k]), k
+    req.close()
