@@ -91,7 +91,11 @@ struct F1Route {
   RowStat* y_stats;           // epilogue 1: [M][N / BN] statistics of C's rows (nullptr: not kept)
 };
 
-template <int BM, int BN, int EPI>
+// NK > 0 (64-row tiles, K = 64 NK): the k loop fully unrolled over three LDS
+// stages, copies issued two steps ahead, each step waiting only for its own
+// stage's copies (an exact wait count and a bare barrier, so the next
+// stage's copies stay in flight); NK = 0: two stages, one step ahead.
+template <int BM, int BN, int EPI, int NK = 0>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ Wt,
                                                            uint16_t* __restrict__ C,
@@ -107,6 +111,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   lds_u16* const A1 = (lds_u16*)A1s;
   lds_u16* const B0 = (lds_u16*)B0s;
   lds_u16* const B1 = (lds_u16*)B1s;
+  constexpr bool kThree = NK > 0;
+  static_assert(!kThree || BM == 64, "three stages fit two blocks a CU only with 64-row tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t A2s[kThree ? BM * GBK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t B2s[kThree ? BN * GBK : 8];
+  lds_u16* const A2 = (lds_u16*)A2s;
+  lds_u16* const B2 = (lds_u16*)B2s;
 
   // XCD-aware tile order: block b runs on XCD b % 8 (the grid is a multiple
   // of 8); XCD x takes tiles x * per_xcd .. , n fastest.
@@ -221,10 +231,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     }
   }
 
-  const int nk = K / GBK;
+  const int nk = kThree ? NK : K / GBK;
   copy_k(0, A0, B0);
+  if (kThree) copy_k(GBK, A1, B1);
   if (EPI == 0 && tid < BN / 4) *reinterpret_cast<f32x4*>(&cs_lds[4 * tid]) = cs_val;
-  __syncthreads();  // k step 0 in buffer 0 (and the prefetched row statistics in)
+  if (!kThree) __syncthreads();  // k step 0 in buffer 0 (and the prefetched row statistics in)
   // f1: each lane's row statistics
   float mu[MT], rstd[MT];
   if (EPI == 0) {
@@ -246,7 +257,29 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       rstd[i] = __builtin_amdgcn_rsqf((m2 + share * dev) * (1.0f / K) + route.eps);
     }
   }
-  for (int kt = 0; kt < nk; kt += 2) {
+  if constexpr (kThree) {
+    // copy instructions a wave issues per stage
+    constexpr int kDma = BM / 32 + BN / 32;
+    lds_u16* const As[3] = {A0, A1, A2};
+    lds_u16* const Bs[3] = {B0, B1, B2};
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      // this wave's copies of step kt have landed (those of step kt + 1 may
+      // still be in flight; vmcnt counts in issue order), then every wave's
+      // have, and every wave is done with step kt - 1, whose buffer the
+      // copies of step kt + 2 refill
+      if (kt + 1 < NK)
+        __builtin_amdgcn_s_waitcnt(0x0070 | (kDma & 15) | ((kDma >> 4) << 14));  // vmcnt(kDma), lgkmcnt(0)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < NK) copy_k((kt + 2) * GBK, As[(kt + 2) % 3], Bs[(kt + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);  // issue the copies before this step's reads
+      mma_k(As[kt % 3], Bs[kt % 3]);
+    }
+    __syncthreads();  // every wave done with the operand buffers the epilogue reuses
+  }
+  for (int kt = 0; !kThree && kt < nk; kt += 2) {
     if (kt + 1 < nk) copy_k((kt + 1) * GBK, A1, B1);
     __builtin_amdgcn_sched_barrier(0);  // issue the copy before this step's reads
     mma_k(A0, B0);
@@ -591,9 +624,16 @@ hipError_t launch_f1_bf16(const void* x, const RowStat* stats, int32_t slots, co
   // without a second block (few new tokens: candidates over a cached history)
   const auto* A = static_cast<const uint16_t*>(x);
   const auto* B = static_cast<const uint16_t*>(w1t);
-  if ((M + 127) / 128 * (N / BN) < 512)
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 0>), dim3(gemm_grid<64, BN>(M, N)), dim3(256), 0, s, A, B,
-                       static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
+#ifndef HSTU_F1_ROW_TILES_AT
+#define HSTU_F1_ROW_TILES_AT 512  // 64-row tiles below this many 128-row blocks
+#endif
+  if ((M + 127) / 128 * (N / BN) < HSTU_F1_ROW_TILES_AT)
+    if (K == 8 * GBK)
+      hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 0, 8>), dim3(gemm_grid<64, BN>(M, N)), dim3(256), 0, s, A, B,
+                         static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 0>), dim3(gemm_grid<64, BN>(M, N)), dim3(256), 0, s, A, B,
+                         static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<128, BN, 0>), dim3(gemm_grid<128, BN>(M, N)), dim3(256), 0, s, A, B,
                        static_cast<uint16_t*>(f.uvqk), nullptr, r, M, N, K);
@@ -617,8 +657,12 @@ hipError_t launch_head_bf16(const HeadArgs& h, hipStream_t s) {
     hipLaunchKernelGGL((gemm_bf16_kernel<128, BN, 2>), dim3(gemm_grid<128, BN>(h.n_rows, N)), dim3(256), 0, s, y,
                        wt, nullptr, nullptr, r, h.n_rows, N, h.d);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 2>), dim3(gemm_grid<64, BN>(h.n_rows, N)), dim3(256), 0, s, y,
-                       wt, nullptr, nullptr, r, h.n_rows, N, h.d);
+    if (h.d == 8 * GBK)
+      hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 2, 8>), dim3(gemm_grid<64, BN>(h.n_rows, N)), dim3(256), 0, s, y,
+                         wt, nullptr, nullptr, r, h.n_rows, N, h.d);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<64, BN, 2>), dim3(gemm_grid<64, BN>(h.n_rows, N)), dim3(256), 0, s, y,
+                         wt, nullptr, nullptr, r, h.n_rows, N, h.d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t outs = static_cast<int64_t>(h.n_rows) * h.tasks;
@@ -639,13 +683,23 @@ hipError_t launch_gemm(int dtype, int epilogue, const void* A, const void* Bm, v
     if (epilogue == 1) {
       F1Route r{};
       r.y_stats = y_stats;
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
-                         static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), r, M, N, K);
+      if (K == 8 * GBK)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 8>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                           static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), r, M, N, K);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                           static_cast<uint16_t*>(C), static_cast<const uint16_t*>(R), r, M, N, K);
     } else {
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 3>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
-                         static_cast<uint16_t*>(C), nullptr, F1Route{}, M, N, K);
+      if (K == 8 * GBK)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 3, 8>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                           static_cast<uint16_t*>(C), nullptr, F1Route{}, M, N, K);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 3>), dim3(gemm_grid<BM, BN>(M, N)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm),
+                           static_cast<uint16_t*>(C), nullptr, F1Route{}, M, N, K);
     }
   } else {
     if (y_stats) return hipErrorInvalidValue;
