@@ -215,6 +215,16 @@ hstu_status staged_host(const void* src, size_t bytes, hipStream_t stream,
   return HSTU_OK;
 }
 
+// the buffer registered with hstu_attn_stamps
+std::mutex g_stamps_mu;
+AttnStamp* g_stamps = nullptr;
+int64_t g_stamps_cap = 0;
+
+AttnStamp* attn_stamps_for(int32_t n_items) {
+  std::lock_guard<std::mutex> lk(g_stamps_mu);
+  return g_stamps && n_items <= g_stamps_cap ? g_stamps : nullptr;
+}
+
 }  // namespace hstu
 
 using namespace hstu;
@@ -576,9 +586,12 @@ static hstu_status fill_keys(AttnLaunch& L, const hstu_plan* p, int dtype, const
 // The attention launch of a plan: one grid, or in split timing mode, when
 // the plan mixes users with and without a cached prefix, its two orders as
 // two grids timed apart (the same items, so the same results).
-static hipError_t run_attention(const hstu_plan* p, const AttnLaunch& L, hipStream_t s) {
+static hipError_t run_attention(const hstu_plan* p, const AttnLaunch& L0, hipStream_t s) {
+  AttnLaunch L = L0;
+  if (L.dtype == HSTU_BF16) L.stamps = attn_stamps_for(p->dev.n_items);
   if (timing_mode() == 2 && !p->items_split.empty()) {
     AttnLaunch A = L;
+    A.stamps = nullptr;
     A.plan.items = p->d_items_split;
     A.plan.n_items = p->n_split_cached;
     hipError_t e = timed(TK_ATTN_CACHED, s, [&] { return launch_attention(A, s); });
@@ -632,6 +645,15 @@ hstu_status attn_fwd_into(const hstu_attn_args* a, void* partials, size_t partia
 }  // namespace hstu
 
 extern "C" {
+
+hstu_status hstu_attn_stamps(void* d_stamps, int64_t capacity) {
+  if (capacity < 0 || (capacity > 0 && !d_stamps)) return fail(HSTU_ERR_INVALID, "hstu_attn_stamps: bad buffer");
+  if (reinterpret_cast<uintptr_t>(d_stamps) % 16) return fail(HSTU_ERR_INVALID, "hstu_attn_stamps: 16-byte alignment");
+  std::lock_guard<std::mutex> lk(g_stamps_mu);
+  g_stamps = capacity > 0 ? static_cast<AttnStamp*>(d_stamps) : nullptr;
+  g_stamps_cap = capacity;
+  return ok();
+}
 
 hstu_status hstu_attn_fwd(const hstu_attn_args* a, hipStream_t stream) {
   return attn_fwd_into(a, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, stream, "hstu_attn_fwd");

@@ -176,6 +176,18 @@ hipError_t launch_gather(int dtype, int32_t B, const int32_t* d_page_table, int3
                          int32_t layer, int32_t num_pages, int32_t H, int32_t dh, int32_t page_size,
                          hipStream_t s);
 
+// One attention block's phase record (hstu_attn_stamps): realtime-clock
+// stamps (100 MHz) at its start, after its set-up (work item, page-table
+// slice, bias, first tiles staged), after its tile loop and at its end, and
+// where it ran.
+struct AttnStamp {
+  uint64_t start, setup_done, loop_done, end;
+  uint32_t hw_id;   // the HW_ID register (CU, shader engine, SIMD, wave slot)
+  uint32_t xcc_id;  // the XCD the block ran on
+  int32_t slot;     // the item's partial slot
+  int32_t tiles;    // key tiles in the item's range
+};
+
 struct AttnLaunch {
   int dtype;
   PlanDev plan;
@@ -194,8 +206,11 @@ struct AttnLaunch {
   const float* rab;
   int32_t num_buckets;
   void* partials;  // fp32 [n_slots][kBlockQ][dh]
+  AttnStamp* stamps;  // per-block phase records [n_items] (nullptr: none)
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+// the phase-record buffer registered with hstu_attn_stamps (nullptr: none)
+AttnStamp* attn_stamps_for(int32_t n_items);
 // hstu_attn_fwd with its fp32 partial tiles in `partials` (partial_bytes
 // long); errors name `who`
 hstu_status attn_fwd_into(const hstu_attn_args* a, void* partials, size_t partial_bytes, hipStream_t stream,

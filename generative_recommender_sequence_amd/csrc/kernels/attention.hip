@@ -117,6 +117,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ float rab_s[kMaxBuckets];  // log2(e) * rab
   __shared__ int32_t pages_lds[PAGED ? kMaxPagesLds : 1];
 
+  const uint64_t t_start = a.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
   const WorkItem w = a.plan.items[blockIdx.x];
   if (w.slot < 0) return;  // padding entry of the dispatch order
   const int h = w.head;
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     copy_tile(t, K0, V0, page_glb);
   }
   __syncthreads();  // rab, page-table slice and tile t staged
+  const uint64_t t_setup = a.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
 
   // two tiles per trip so that each half names its buffers statically
   while (t < w.tile_end) {
@@ -358,6 +360,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     t = tn;
   }
 
+  const uint64_t t_loop = a.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
   // ---- partial tile [BQ][DH] fp32 (times log2 e).  A lane holds column
   // 32 nt + l32 of rows 8(r/4)+4g+r%4; the tile goes through LDS (the four
   // K/V buffers, free after the last barrier, 32 rows each) so that whole
@@ -384,6 +387,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a) {
     if (row < w.count)
       *reinterpret_cast<f32x4*>(out + row * DH + 4 * sch) =
           *(const __attribute__((address_space(3))) f32x4*)(stage_row(row) + 4 * sch);
+  }
+  if (a.stamps && tid == 0) {
+    AttnStamp st;
+    st.start = t_start;
+    st.setup_done = t_setup;
+    st.loop_done = t_loop;
+    st.end = __builtin_amdgcn_s_memrealtime();
+    st.hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID, all 32 bits
+    st.xcc_id = __builtin_amdgcn_s_getreg((3 << 11) | 20);   // XCC_ID[3:0]
+    st.slot = w.slot;
+    st.tiles = w.tile_end - w.tile_begin;
+    a.stamps[blockIdx.x] = st;
   }
 }
 

@@ -126,6 +126,7 @@ SIGNATURES = {
     "hstu_batcher_next": (c_i32, [c_vp, c_i64, P_i64, c_i32, P_i32, P_i64]),
     "hstu_batcher_pending": (c_i32, [c_vp, P_i32]),
     "hstu_timing_enable": (c_i32, [c_i32]),
+    "hstu_attn_stamps": (c_i32, [c_vp, c_i64]),
     "hstu_ceiling_mfma": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
     "hstu_ceiling_read": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "hstu_ceiling_copy": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
@@ -545,3 +546,12 @@ def hstu_ceiling_read(src: int, nbytes: int, out: int, stream: int):
 
 def hstu_ceiling_copy(src: int, dst: int, nbytes: int, stream: int):
     _check(lib().hstu_ceiling_copy(src, dst, nbytes, stream), "hstu_ceiling_copy")
+
+
+ATTN_STAMP_DTYPE = np.dtype([("start", "<u8"), ("setup_done", "<u8"), ("loop_done", "<u8"), ("end", "<u8"),
+                             ("hw_id", "<u4"), ("xcc_id", "<u4"), ("slot", "<i4"), ("tiles", "<i4")])
+
+
+def hstu_attn_stamps(d_stamps: int, capacity: int):
+    """Registers (capacity > 0) or clears the attention phase-record buffer."""
+    _check(lib().hstu_attn_stamps(d_stamps or None, capacity), "hstu_attn_stamps")

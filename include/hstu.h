@@ -523,6 +523,19 @@ hstu_status hstu_timing_enable(int32_t enable);
  * INVALID for an unknown name. */
 hstu_status hstu_timing_read(const char *kernel, int32_t *launches, double *total_ms);
 
+/* Phase records of the bf16 attention: with d_stamps (device, 16-byte
+ * aligned) registered for `capacity` records, every later single-grid bf16
+ * attention launch of a plan with at most `capacity` blocks writes, for
+ * block b, record b (48 bytes): uint64 start, setup_done, loop_done, end
+ * (the 100 MHz realtime clock at the block's start, after its set-up, after
+ * its key-tile loop, at its end), uint32 hw_id (the HW_ID register: CU in
+ * bits 8-11, shader engine in bits 13-14), uint32 xcc_id (the XCD), int32
+ * slot and int32 tiles (the work item's partial slot and key-tile range;
+ * padding blocks write nothing).  Each launch overwrites the records; the
+ * caller reads them after synchronising.  capacity 0 (d_stamps NULL)
+ * switches the records off.  Costs one uniform branch a block when off. */
+hstu_status hstu_attn_stamps(void *d_stamps, int64_t capacity);
+
 /* Achievable ceilings of the two resources the layer is bound by (the
  * benchmark quotes roofline fractions against these beside the vendor
  * peaks; the pages state their target as a fraction of the HBM / MFMA

@@ -186,3 +186,13 @@ def test_plan_items_cover_visible_tiles_within_page_limit(case):
                 got += [t for t in want if tb <= t < te]
                 assert tb in want and te - 1 in want        # pieces start and end on visible tiles
             assert got == want, (qb, hd)
+
+
+def test_attn_stamps_validation():
+    """The phase-record registration rejects a negative capacity, a missing or
+    misaligned buffer, and clears with capacity 0 (no device access)."""
+    lib = hstu.lib()
+    assert lib.hstu_attn_stamps(None, -1) == hstu.HSTU_ERR_INVALID
+    assert lib.hstu_attn_stamps(None, 4) == hstu.HSTU_ERR_INVALID
+    assert lib.hstu_attn_stamps(0x1008, 4) == hstu.HSTU_ERR_INVALID
+    assert lib.hstu_attn_stamps(None, 0) == hstu.HSTU_OK

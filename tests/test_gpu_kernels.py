@@ -322,3 +322,50 @@ def test_attention_split_timing_launch_is_identical():
     assert (n_c, n_p, n_a) == (1, 1, 0)
     assert torch.equal(o1, o2)
     req.close()
+
+
+def test_attention_phase_records():
+    """With a phase-record buffer registered, every block of the bf16
+    attention writes its record (ordered stamps, its work item's slot and
+    tile range) and the output is byte-identical to a launch without one."""
+    new_len, cached_len, n_targets = [64, 700, 64, 300], [1500, 0, 900, 0], [64, 64, 64, 17]
+    say("attention phase records")
+    rng = np.random.default_rng(37)
+    H, dh, dtype = 2, 128, HSTU_BF16
+    q, k, v, rab, L, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, 32, new_len, cached_len,
+                                                            n_targets, 4)
+    req = runtime.prepare_attn(cache, users, new_len, n_targets, None, max_pages, H, dh)
+    items = hstu.hstu_plan_get_items(req.plan)
+    qd = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    rabd = torch.from_numpy(rab).cuda()
+    o1 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
+    n = len(items)
+    rec = hstu.ATTN_STAMP_DTYPE.itemsize
+    buf = torch.zeros(n * rec // 8, dtype=torch.int64, device="cuda")
+    hstu.hstu_attn_stamps(buf.data_ptr(), n)
+    try:
+        o2 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
+        torch.cuda.synchronize()
+    finally:
+        hstu.hstu_attn_stamps(0, 0)
+    a = np.frombuffer(buf.cpu().numpy().tobytes(), dtype=hstu.ATTN_STAMP_DTYPE)
+    real = items[:, 5] >= 0
+    assert torch.equal(o1, o2)
+    assert (a["end"][~real] == 0).all()
+    r = a[real]
+    assert (r["start"] > 0).all()
+    assert (r["start"] <= r["setup_done"]).all() and (r["setup_done"] <= r["loop_done"]).all()
+    assert (r["loop_done"] <= r["end"]).all()
+    np.testing.assert_array_equal(r["slot"], items[real, 5])
+    np.testing.assert_array_equal(r["tiles"], items[real, 4] - items[real, 3])
+    assert (r["xcc_id"] < 8).all()
+    # a record buffer smaller than the plan is not used
+    small = torch.zeros(8, dtype=torch.int64, device="cuda")
+    hstu.hstu_attn_stamps(small.data_ptr(), 1)
+    try:
+        o3 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
+        torch.cuda.synchronize()
+    finally:
+        hstu.hstu_attn_stamps(0, 0)
+    assert torch.equal(o1, o3) and int(small.abs().sum()) == 0
+    req.close()
