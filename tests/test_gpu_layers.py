@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from generative_recommender_sequence_amd import runtime
+from generative_recommender_sequence_amd import hstu, runtime
 from generative_recommender_sequence_amd.workloads import CONFIGS, generate, round_bf16, small_config
 from gpu_checks import TOL, check_layers, rel, run_layers_with_taps, say, to64
 
@@ -336,5 +336,34 @@ def test_attention_output_layernorm_edge_bf16(kind):
     say(f"  o rows: median |mean|/std {np.median(np.abs(mu) / np.maximum(sd, 1e-30)):.1f}, "
         f"median variance {np.median(sd ** 2):.2e}")
     worst = check_layers(scn, req, per, [0, 1, 2], f"ln-o-{kind}")
+    _assert_within(worst, TOL[scn.dtype])
+    req.close()
+
+
+def test_layer_longest_cached_user_wide_model_bf16():
+    """The row that sums the most partial tiles: one user at the longest
+    supported sequence (65,471 cached positions + 64 candidates = 65,535) in
+    16-token pages, d_model 1024, one layer.  Each candidate row's output is
+    the key-order sum of several hundred pieces' fp32 partial tiles; the
+    layer (through LN(o), the gate and f2) must stay within the bound."""
+    say("longest cached user, wide model bf16")
+    hist = [65471]
+    cfg = small_config(dtype="bf16", d_model=1024, num_heads=2, head_dim=128, num_layers=1, n_targets=64,
+                       cache="hit", page_size=16)
+    w = generate(cfg, 8, batch=1, hist_override=hist)
+    w.hit = np.ones(1, bool)
+    w.prefill_order = np.arange(1, dtype=np.int32)
+    w.num_pages = -(-(hist[0] + 64) // 16) + 3
+    w.page_perm = np.random.default_rng(9).permutation(w.num_pages).astype(np.int32)
+    w.cfg = dataclasses.replace(cfg, batch=1)
+    scn = runtime.Scenario(w)
+    scn.prefill()
+    req, x = scn.make_request()
+    items = hstu.hstu_plan_get_items(req.plan)
+    pieces = int((items[:, 5] >= 0).sum())
+    per = run_layers_with_taps(scn, req, x)
+    worst = check_layers(scn, req, per, [0], "longest")
+    say(f"  {pieces} pieces over 2 heads")
+    assert pieces >= 64
     _assert_within(worst, TOL[scn.dtype])
     req.close()
