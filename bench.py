@@ -263,35 +263,43 @@ class Run:
             torch.cuda.synchronize()
             hstu.hstu_attn_stamps(0, 0)
         a = np.frombuffer(buf.cpu().numpy().tobytes()[:n * rec], dtype=hstu.ATTN_STAMP_DTYPE)
-        a = a[a["end"] > 0]
-        if len(a) == 0:
-            return None
-        ns = 10.0  # the realtime counter runs at 100 MHz
-        t0 = int(a["start"].min())
-        span = (int(a["end"].max()) - t0) * ns / 1000.0
-        setup = (a["setup_done"] - a["start"]) * ns / 1000.0
-        loop = (a["loop_done"] - a["setup_done"]) * ns / 1000.0
-        write = (a["end"] - a["loop_done"]) * ns / 1000.0
-        tiles = np.maximum(a["tiles"], 1)
-        cu = a["xcc_id"].astype(np.int64) * 256 + ((a["hw_id"] >> 8) & 0xFF)
-        n_cu = len(np.unique(cu))
-        busy = float(((a["end"] - a["start"]) * ns / 1000.0).sum())
-        xcd_end = {int(x): round((int(a["end"][a["xcc_id"] == x].max()) - t0) * ns / 1000.0, 2)
-                   for x in np.unique(a["xcc_id"])}
-        cu_end = np.array([(int(a["end"][cu == c].max()) - t0) * ns / 1000.0 for c in np.unique(cu)])
+        return summarize_phases(a)
 
-        def q(v):
-            return {"p10": round(float(np.percentile(v, 10)), 3), "p50": round(float(np.percentile(v, 50)), 3),
-                    "p90": round(float(np.percentile(v, 90)), 3), "max": round(float(v.max()), 3)}
-        return {"blocks": int(len(a)), "cus_used": n_cu, "span_us": round(span, 2),
-                "setup_us": q(setup), "tile_loop_us_per_tile": q(loop / tiles), "tiles_per_block": q(a["tiles"]),
-                "write_us": q(write),
-                "busy_share": round(busy / (2 * max(n_cu, 1) * span), 3) if span > 0 else None,
-                "xcd_last_end_us": xcd_end,
-                "cu_last_end_us": q(cu_end),
-                "note": ("realtime-clock stamps (10 ns) written by every attention block of one launch (the last "
-                         "layer of a request); busy_share = summed block time / (2 resident blocks x CUs used x "
-                         "span)")}
+
+def summarize_phases(a):
+    """Summary of one attention launch's phase records (hstu_attn_stamps):
+    set-up, per-tile loop and write times (p10/p50/p90/max over blocks), the
+    launch span, the CUs used, when each XCD and each CU ran out of work, and
+    the share of the span the CUs' two block slots were busy."""
+    a = a[a["end"] > 0]
+    if len(a) == 0:
+        return None
+    ns = 10.0  # the realtime counter runs at 100 MHz
+    t0 = int(a["start"].min())
+    span = (int(a["end"].max()) - t0) * ns / 1000.0
+    setup = (a["setup_done"] - a["start"]) * ns / 1000.0
+    loop = (a["loop_done"] - a["setup_done"]) * ns / 1000.0
+    write = (a["end"] - a["loop_done"]) * ns / 1000.0
+    tiles = np.maximum(a["tiles"], 1)
+    cu = a["xcc_id"].astype(np.int64) * 256 + ((a["hw_id"] >> 8) & 0xFF)
+    n_cu = len(np.unique(cu))
+    busy = float(((a["end"] - a["start"]) * ns / 1000.0).sum())
+    xcd_end = {int(x): round((int(a["end"][a["xcc_id"] == x].max()) - t0) * ns / 1000.0, 2)
+               for x in np.unique(a["xcc_id"])}
+    cu_end = np.array([(int(a["end"][cu == c].max()) - t0) * ns / 1000.0 for c in np.unique(cu)])
+
+    def q(v):
+        return {"p10": round(float(np.percentile(v, 10)), 3), "p50": round(float(np.percentile(v, 50)), 3),
+                "p90": round(float(np.percentile(v, 90)), 3), "max": round(float(v.max()), 3)}
+    return {"blocks": int(len(a)), "cus_used": n_cu, "span_us": round(span, 2),
+            "setup_us": q(setup), "tile_loop_us_per_tile": q(loop / tiles), "tiles_per_block": q(a["tiles"]),
+            "write_us": q(write),
+            "busy_share": round(busy / (2 * max(n_cu, 1) * span), 3) if span > 0 else None,
+            "xcd_last_end_us": xcd_end,
+            "cu_last_end_us": q(cu_end),
+            "note": ("realtime-clock stamps (10 ns) written by every attention block of one launch (the last "
+                     "layer of a request); busy_share = summed block time / (2 resident blocks x CUs used x "
+                     "span)")}
 
 
 def measure(name, seed, steps, warmup, latency_n, ceil, split=False):
