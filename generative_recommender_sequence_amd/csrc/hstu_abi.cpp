@@ -219,10 +219,13 @@ hstu_status staged_host(const void* src, size_t bytes, hipStream_t stream,
 std::mutex g_stamps_mu;
 AttnStamp* g_stamps = nullptr;
 int64_t g_stamps_cap = 0;
+int g_stamps_dev = -1;  // the device current when the buffer was registered
 
 AttnStamp* attn_stamps_for(int32_t n_items) {
   std::lock_guard<std::mutex> lk(g_stamps_mu);
-  return g_stamps && n_items <= g_stamps_cap ? g_stamps : nullptr;
+  if (!g_stamps || n_items > g_stamps_cap) return nullptr;
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == g_stamps_dev ? g_stamps : nullptr;
 }
 
 }  // namespace hstu
@@ -649,9 +652,15 @@ extern "C" {
 hstu_status hstu_attn_stamps(void* d_stamps, int64_t capacity) {
   if (capacity < 0 || (capacity > 0 && !d_stamps)) return fail(HSTU_ERR_INVALID, "hstu_attn_stamps: bad buffer");
   if (reinterpret_cast<uintptr_t>(d_stamps) % 16) return fail(HSTU_ERR_INVALID, "hstu_attn_stamps: 16-byte alignment");
+  int dev = -1;
+  if (capacity > 0) {
+    hstu_status st = check_hip(hipGetDevice(&dev), "hstu_attn_stamps");
+    if (st != HSTU_OK) return st;
+  }
   std::lock_guard<std::mutex> lk(g_stamps_mu);
   g_stamps = capacity > 0 ? static_cast<AttnStamp*>(d_stamps) : nullptr;
   g_stamps_cap = capacity;
+  g_stamps_dev = dev;
   return ok();
 }
 

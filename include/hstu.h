@@ -532,8 +532,10 @@ hstu_status hstu_timing_read(const char *kernel, int32_t *launches, double *tota
  * bits 8-11, shader engine in bits 13-14), uint32 xcc_id (the XCD), int32
  * slot and int32 tiles (the work item's partial slot and key-tile range;
  * padding blocks write nothing).  Each launch overwrites the records; the
- * caller reads them after synchronising.  capacity 0 (d_stamps NULL)
- * switches the records off.  Costs one uniform branch a block when off. */
+ * caller reads them after synchronising.  The buffer belongs to the device
+ * current at registration; launches on other devices write no records.
+ * capacity 0 (d_stamps NULL) switches the records off.  Costs one uniform
+ * branch a block when off. */
 hstu_status hstu_attn_stamps(void *d_stamps, int64_t capacity);
 
 /* Achievable ceilings of the two resources the layer is bound by (the
