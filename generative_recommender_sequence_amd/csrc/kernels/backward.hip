@@ -342,15 +342,18 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ p
 // ---------------------------------------------------------------------------
 // attention, per 64-key block: dK, dV and the rab gradient
 // ---------------------------------------------------------------------------
-// Two key groups of 32, each taken by two waves that split the head dims of
-// dK and dV between them (and both compute S and dP), so that a wave fits in
-// half the register file and two blocks share a CU; the block's K and V rows
-// sit in LDS.  A step covers 32 queries.  The rab gradient is summed per
-// distance i - j in LDS (one wave per key group gathers its 32 x 32 pairs by
-// distance across lanes and adds one atomic per distance; when its pairs
-// fall in at most four buckets it adds one wave sum per bucket), distances
-// past the LDS window (ragged tail steps) straight into their bucket; the
-// sums are folded into buckets and written as this item's partial.
+// Two key groups of 32, each taken by two waves with split roles, so that
+// each pair's S and dP are computed once and a wave fits in half the
+// register file (two blocks share a CU); the block's K and V rows sit in
+// LDS.  A step covers 32 queries.  Wave A of a group computes z = S + bias,
+// passes it to wave B through the group's LDS scratch, and accumulates dV
+// over all head dims; wave B computes dP, forms dz from it and z, sums the
+// rab gradient and accumulates dK over all head dims.  The rab gradient is
+// summed per distance i - j in LDS (wave B gathers its 32 x 32 pairs by
+// distance across lanes and adds one sum per distance; when its pairs fall
+// in at most four buckets it adds one wave sum per bucket), distances past
+// the LDS window (ragged tail steps) straight into their bucket; the sums
+// are folded into buckets and written as this item's partial.
 constexpr int KB = kBwdKeyBlock;  // keys per item: 2 groups of 32, each split over two waves by head dims
 constexpr int QT = 32;            // queries per step
 constexpr int kTab = QT + KB;     // distances per step (95 used)
@@ -385,8 +388,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
   const int64_t ST = 4 * static_cast<int64_t>(inner);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = uniform(tid >> 6);
-  const int kg = wave >> 1, hh = wave & 1;  // key group; half of the head dims this wave accumulates
-  const bool do_rab = hh == 0;              // one wave of each key group sums the rab gradient
+  const int kg = wave >> 1;                 // key group
+  const bool role_b = (wave & 1) != 0;      // A: z and dV; B: dP, dz, the rab gradient and dK
   const int kw0 = k0 + 32 * kg;
   const int key = kw0 + l32;
   const int ndist = L - k0;  // distances 0 .. L - 1 - k0 can occur
@@ -406,10 +409,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
     dma16(src + 3 * inner, Kt + (16 * wave + 4 * i) * DH);
     dma16(src + 1 * inner, Vt + (16 * wave + 4 * i) * DH);
   }
-  // dV and dK of this wave's 32 keys over head dims 64 hh .. 64 hh + 63
-  f32x16 dv_acc[2], dk_acc[2];
+  // dV (wave A) or dK (wave B) of this group's 32 keys over all head dims
+  f32x16 gacc[DH / 32];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) dv_acc[t] = dk_acc[t] = f32x16{};
+  for (int t = 0; t < DH / 32; ++t) gacc[t] = f32x16{};
 
   // query steps that see some key of the block
   const int kb_end = min(k0 + KB, L);
@@ -436,22 +439,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       bias[tid] = d < 0 ? 0.f : b.rab[rel_bucket(d, nb)];
     }
   };
-  // transposed-read addresses of this wave's two column blocks (2 hh, 2 hh + 1),
-  // selected once (a run-time index into the helper's table would go to scratch)
-  int tra[2][2];
-  {
-    TrAddr tr;
-    tr.init(lane);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) tra[r][t] = hh ? tr.a[r][2 + t] : tr.a[r][t];
-  }
-  auto tr_read = [&](const lds_u16* T, int t, int ks) {
-    u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(T + tra[0][t] + 16 * ks * DH));
-    u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(T + tra[1][t] + 16 * ks * DH));
-    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-  };
+  // transposed-read addresses of the four column blocks
+  TrAddr tr;
+  tr.init(lane);
   // A operand of S: query row perm(l32); B operand: this lane's key row
   // 32 kg + l32; chunk (2s + g) of each, swizzled (formed per use to save registers)
   const int qrow = perm(l32), krow = 32 * kg + l32;
@@ -492,23 +482,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       }
     }
   };
-  // register r holds query q0 + 16 (r / 8) + 8 g + r % 8 against this lane's key.
-  // Wave-uniform cases, each a straight loop: every pair visible in one
-  // bucket (one wave sum) or in at most four (one wave sum per bucket, split
-  // at the bucket edges), every pair visible (sums per distance), or masked
-  // (masked pairs count zero, then sums per distance).
-  auto elementwise = [&](int q0, f32x16& sacc, f32x16& pacc, const float* bias) {
-    const int qh = q0;
+  // register r holds query q0 + 16 (r / 8) + 8 g + r % 8 against this lane's
+  // key, and z[r] the pair's q.k + rab.  Masked pairs count zero.
+  auto visible = [&](int qh, int r) {
+    const int i = qh + 16 * (r >> 3) + 8 * g + (r & 7);
+    return (i < L) & (key < L) & ((key == i) | ((key < i) & (key < hist)));
+  };
+  auto full_step = [&](int qh) { return kw0 + 31 < qh && kw0 + 31 < hist && qh + 32 <= L && kw0 + 31 < L; };
+  // wave A: z into the A operands' weights p = SiLU(z) / n
+  auto weights_p = [&](int qh, f32x16& z) {
+    if (full_step(qh)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = z[r] * sigmoid(z[r]) * inv_n;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = visible(qh, r) ? z[r] * sigmoid(z[r]) * inv_n : 0.f;
+    }
+  };
+  // wave B: dP into dz = dP / n * SiLU'(z), and the rab gradient.  Wave-uniform
+  // cases, each a straight loop: every pair visible in one bucket (one wave
+  // sum) or in at most four (one wave sum per bucket, split at the bucket
+  // edges), every pair visible (sums per distance), or masked (sums per
+  // distance).
+  auto gradient_dz = [&](int qh, const f32x16& z, f32x16& pacc) {
     const int dmin = qh - (kw0 + 31), dmax = qh + 31 - kw0;
-    const bool full = kw0 + 31 < qh && kw0 + 31 < hist && qh + 32 <= L && kw0 + 31 < L;
+    const bool full = full_step(qh);
     const bool uni = full && rel_bucket(dmin, nb) == rel_bucket(dmax, nb);
-    const int tb = (KB - 1) - (key - k0);  // table entry of register 0
-    const int sb = qh - key;               // distance of register 0
-    auto pair = [&](int r, float& p, float& dz) {
-      const float z = sacc[r] + bias[tb + 16 * (r >> 3) + 8 * g + (r & 7)];
-      const float sg = sigmoid(z);
-      p = z * sg * inv_n;
-      dz = pacc[r] * inv_n * sg * (1.0f + z * (1.0f - sg));
+    const int sb = qh - key;  // distance of register 0
+    auto dz_of = [&](int r) {
+      const float sg = sigmoid(z[r]);
+      return pacc[r] * inv_n * sg * (1.0f + z[r] * (1.0f - sg));
     };
     // up to four buckets: t[k] is the first distance of bucket blo + 1 + k
     const int blo = full ? rel_bucket(dmin, nb) : 0;
@@ -518,24 +521,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       float dsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p, dz;
-        pair(r, p, dz);
-        sacc[r] = p;
-        pacc[r] = dz;
-        dsum += dz;
+        pacc[r] = dz_of(r);
+        dsum += pacc[r];
       }
-      if (do_rab) {
-        dsum = wave_sum(dsum);
-        if (lane == 0) drab_s[kg][bhi] += dsum;
-      }
-    } else if (few && !do_rab) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p, dz;
-        pair(r, p, dz);
-        sacc[r] = p;
-        pacc[r] = dz;
-      }
+      dsum = wave_sum(dsum);
+      if (lane == 0) drab_s[kg][bhi] += dsum;
     } else if (few) {
       int t[3];
 #pragma unroll
@@ -554,9 +544,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       float s_all = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p, dz;
-        pair(r, p, dz);
-        sacc[r] = p;
+        const float dz = dz_of(r);
         pacc[r] = dz;
         const int dd = sb + 16 * (r >> 3) + 8 * g + (r & 7);
         s_all += dz;
@@ -576,55 +564,64 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       }
     } else if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p, dz;
-        pair(r, p, dz);
-        sacc[r] = p;
-        pacc[r] = dz;
-      }
-      if (do_rab) diag_add(qh, pacc);
+      for (int r = 0; r < 16; ++r) pacc[r] = dz_of(r);
+      diag_add(qh, pacc);
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p, dz;
-        pair(r, p, dz);
-        const int i = qh + 16 * (r >> 3) + 8 * g + (r & 7);
-        const bool vis = (i < L) & (key < L) & ((key == i) | ((key < i) & (key < hist)));
-        sacc[r] = vis ? p : 0.f;
-        pacc[r] = vis ? dz : 0.f;
-      }
-      if (do_rab) diag_add(qh, pacc);
+      for (int r = 0; r < 16; ++r) pacc[r] = visible(qh, r) ? dz_of(r) : 0.f;
+      diag_add(qh, pacc);
     }
   };
-  // dV += P^T dO, dK += dZ^T Q over the step's 32 queries, for this wave's
-  // half of the head dims (column blocks 2 hh and 2 hh + 1)
-  auto accumulate = [&](const f32x16& sacc, const f32x16& pacc, const lds_u16* Qs, const lds_u16* Ds) {
+  // wave A: dV += P^T dO; wave B: dK += dZ^T Q, over the step's 32 queries
+  // and all head dims
+  auto accumulate = [&](const f32x16& w, const lds_u16* T) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pa, za;
+      bf16x8 wa;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pa[e] = static_cast<__bf16>(sacc[8 * ks + e]);
-        za[e] = static_cast<__bf16>(pacc[8 * ks + e]);
-      }
+      for (int e = 0; e < 8; ++e) wa[e] = static_cast<__bf16>(w[8 * ks + e]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_read(Ds, t, ks), dv_acc[t], 0, 0, 0);
-        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, tr_read(Qs, t, ks), dk_acc[t], 0, 0, 0);
-      }
+      for (int t = 0; t < DH / 32; ++t)
+        gacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, tr.read(T, t, ks), gacc[t], 0, 0, 0);
     }
   };
-  // S and dP over all head dims (both waves of a key group compute them)
+  // z (wave A) or dP (wave B) over all head dims; z passes through the key
+  // group's scratch, in the layout the distance sums use (wave B reads it
+  // before its own sums overwrite it; wave A writes the next step's after
+  // the step's closing barrier).  Every wave reaches the barrier in between.
   auto step = [&](int q0, const lds_u16* Qs, const lds_u16* Ds, const float* bias) {
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    const bool active = kw0 < L;
+    f32x16 acc = f32x16{};
+    if (active) {
+      const lds_u16* Xs = role_b ? Ds : Qs;
+      const lds_u16* Ys = role_b ? Vt : Kt;
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
-      const int qa_s = qbase + 8 * ((2 * s + g) ^ qx), ka_s = kbase + 8 * ((2 * s + g) ^ kx);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qs + qa_s), lds_row8(Kt + ka_s), sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Ds + qa_s), lds_row8(Vt + ka_s), pacc, 0, 0, 0);
+      for (int s = 0; s < DH / 16; ++s) {
+        const int qa_s = qbase + 8 * ((2 * s + g) ^ qx), ka_s = kbase + 8 * ((2 * s + g) ^ kx);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Xs + qa_s), lds_row8(Ys + ka_s), acc, 0, 0, 0);
+      }
+      if (!role_b) {
+        const int tb = (KB - 1) - (key - k0);  // table entry of register 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[r] += bias[tb + 16 * (r >> 3) + 8 * g + (r & 7)];
+          scr[(16 * (r >> 3) + 8 * g + (r & 7)) * 33 + l32] = acc[r];
+        }
+      }
     }
-    elementwise(q0, sacc, pacc, bias);
-    accumulate(sacc, pacc, Qs, Ds);
+    __syncthreads();  // z of the step in the scratch
+    if (active) {
+      if (!role_b) {
+        weights_p(q0, acc);
+        accumulate(acc, Ds);
+      } else {
+        f32x16 z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = scr[(16 * (r >> 3) + 8 * g + (r & 7)) * 33 + l32];
+        gradient_dz(q0, z, acc);
+        accumulate(acc, Qs);
+      }
+    }
   };
 
   int q0 = (k0 / QT) * QT;
@@ -642,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       copy_tile(qn, Q1, D1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kw0 < L) step(q0, Q0, D0, bias0);
+    step(q0, Q0, D0, bias0);
     __syncthreads();
     if (qn >= L) break;
     q0 = qn;
@@ -653,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
       copy_tile(qn, Q0, D0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kw0 < L) step(q0, Q1, D1, bias1);
+    step(q0, Q1, D1, bias1);
     __syncthreads();
     q0 = qn;
   }
@@ -677,17 +674,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(BwdLaunch b) {
     for (int d = first_at_least(k); d < d1; ++d) sum += dist_s[0][d] + dist_s[1][d];
     b.drab_partial[static_cast<int64_t>(blockIdx.x) * nb + k] = sum;
   }
-  // rows (keys) 8 (r / 4) + 4 g + r % 4 of this wave's 32, column 32 (2 hh + t) + l32
+  // rows (keys) 8 (r / 4) + 4 g + r % 4 of this group's 32, column 32 t + l32:
+  // dV (chunk 1 of da) from wave A, dK (chunk 3) from wave B
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < DH / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (kk < L) {
-        uint16_t* dst = b.da + (row0 + kk) * ST + h * DH + 32 * (2 * hh + t) + l32;
-        dst[1 * inner] = f2bf(dv_acc[t][r]);
-        dst[3 * inner] = f2bf(dk_acc[t][r]);
-      }
+      if (kk < L)
+        b.da[(row0 + kk) * ST + (role_b ? 3 : 1) * inner + h * DH + 32 * t + l32] = f2bf(gacc[t][r]);
     }
 }
 
