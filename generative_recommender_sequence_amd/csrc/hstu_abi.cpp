@@ -58,14 +58,6 @@ constexpr int kMinPieceTiles = HSTU_MIN_PIECE_TILES;
 constexpr int kMaxPieceTiles = 256;  // bounds a work item's staged page-table slice
 constexpr int kXcds = 8;             // workgroups are dealt to the 8 XCDs round-robin
 
-bool tile_visible(int64_t k0, int64_t qa, int64_t qe, int64_t hist) {
-  // some key j in [k0, k0+kTileK) visible to some query i in [qa, qe):
-  // either j == i for some i, or j < i and j < hist
-  int64_t k1 = k0 + kTileK;
-  if (k0 < qe && qa < k1) return true;
-  return k0 < hist && k0 < qe - 1;
-}
-
 // Pinned staging for host-to-device uploads, so they are truly asynchronous
 // and the host can plan the next request while the GPU runs this one.  A
 // small ring of pinned buffers, each reused only after its previous copy has
@@ -100,53 +92,79 @@ StagingRing& staging() {
 // (ties keep the group order), so that its last slots free together; XCD
 // x's k-th piece sits at index 8k + x and short queues are padded with no-op
 // entries (slot -1), so out grows by a multiple of 8.
-void dispatch_order(const std::vector<std::pair<int32_t, WorkItem>>& pieces, int32_t B, int32_t H,
-                    std::vector<WorkItem>& out) {
-  std::vector<std::vector<std::pair<int32_t, WorkItem>>> groups;
+void dispatch_order(const std::vector<std::pair<int32_t, WorkItem>>& pieces, const std::vector<int32_t>& sel,
+                    int32_t B, int32_t H, std::vector<WorkItem>& out) {
+  // pieces are handled by index (sel: the pieces to order, in input order)
+  const int32_t n = static_cast<int32_t>(sel.size());
+  auto tiles = [&](int32_t i) { return pieces[i].first; };
+  // groups in order of first appearance, each group's pieces in input order
+  std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1), gfirst, gcount;
   std::vector<int64_t> gcost;
-  std::vector<int32_t> gid(static_cast<size_t>(B) * H, -1);
+  std::vector<int32_t> pg(n);
   int64_t all = 0;
-  for (const auto& pc : pieces) {
-    int32_t key = pc.second.user * H + pc.second.head;
-    if (gid[key] < 0) {
-      gid[key] = static_cast<int32_t>(groups.size());
-      groups.emplace_back();
+  for (int32_t k = 0; k < n; ++k) {
+    const WorkItem& w = pieces[sel[k]].second;
+    int32_t& g = gid[static_cast<size_t>(w.user) * H + w.head];
+    if (g < 0) {
+      g = static_cast<int32_t>(gcost.size());
       gcost.push_back(0);
+      gcount.push_back(0);
     }
-    groups[gid[key]].push_back(pc);
-    gcost[gid[key]] += pc.first;
-    all += pc.first;
+    pg[k] = g;
+    gcost[g] += tiles(sel[k]);
+    ++gcount[g];
+    all += tiles(sel[k]);
   }
+  const int32_t ng = static_cast<int32_t>(gcost.size());
+  gfirst.assign(ng + 1, 0);
+  for (int32_t g = 0; g < ng; ++g) gfirst[g + 1] = gfirst[g] + gcount[g];
+  std::vector<int32_t> byg(n), fill(gfirst.begin(), gfirst.end() - 1);
+  for (int32_t k = 0; k < n; ++k) byg[fill[pg[k]]++] = sel[k];
   const int64_t share = (all + kXcds - 1) / kXcds;
-  std::vector<int32_t> gorder(groups.size());
+  // Sorts run on 64-bit keys (visible tiles descending in the high half, the
+  // tie-break ascending in the low half): the stable orders, without the
+  // temporary buffers of std::stable_sort or indirect compares.
+  auto key = [&](int32_t tiles_, int32_t tie) {
+    return (static_cast<uint64_t>(static_cast<uint32_t>(INT32_MAX - tiles_)) << 32) | static_cast<uint32_t>(tie);
+  };
+  std::vector<int32_t> gorder(ng);
   std::iota(gorder.begin(), gorder.end(), 0);
-  std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
-  // (visible tiles, arrival order, item) per XCD
-  std::vector<std::vector<std::tuple<int32_t, int32_t, WorkItem>>> q(kXcds);
+  std::sort(gorder.begin(), gorder.end(),
+            [&](int32_t a, int32_t b) { return gcost[a] != gcost[b] ? gcost[a] > gcost[b] : a < b; });
+  // per XCD, keys of (visible tiles, assignment order); seq_piece maps the
+  // assignment order back to the piece
+  std::vector<std::vector<uint64_t>> q(kXcds);
+  for (auto& qq : q) qq.reserve(static_cast<size_t>(n) / kXcds + 1);
+  std::vector<int32_t> seq_piece;
+  seq_piece.reserve(n);
+  std::vector<uint64_t> gk;
   std::vector<int64_t> load(kXcds, 0);
-  int32_t seq = 0;
   auto least = [&]() { return static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin()); };
   for (int32_t gi : gorder) {
-    auto& grp = groups[gi];
-    std::stable_sort(grp.begin(), grp.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+    // a group's pieces, longest first, ties in input order (increasing index)
+    gk.clear();
+    for (int32_t k = gfirst[gi]; k < gfirst[gi + 1]; ++k) gk.push_back(key(tiles(byg[k]), byg[k]));
+    std::sort(gk.begin(), gk.end());
     const int home = least();
-    for (const auto& pc : grp) {
-      const int x = load[home] + pc.first <= share ? home : least();
-      q[x].emplace_back(pc.first, seq++, pc.second);
-      load[x] += pc.first;
+    for (uint64_t kv : gk) {
+      const int32_t i = static_cast<int32_t>(kv & 0xFFFFFFFFu);
+      const int x = load[home] + tiles(i) <= share ? home : least();
+      q[x].push_back(key(tiles(i), static_cast<int32_t>(seq_piece.size())));
+      seq_piece.push_back(i);
+      load[x] += tiles(i);
     }
   }
   size_t depth = 0;
   for (auto& qq : q) {
-    std::sort(qq.begin(), qq.end(), [](const auto& a, const auto& b) {
-      return std::get<0>(a) != std::get<0>(b) ? std::get<0>(a) > std::get<0>(b) : std::get<1>(a) < std::get<1>(b);
-    });
+    std::sort(qq.begin(), qq.end());
     depth = std::max(depth, qq.size());
   }
   WorkItem pad{};
   pad.slot = -1;
+  out.reserve(out.size() + depth * kXcds);
   for (size_t k = 0; k < depth; ++k)
-    for (int x = 0; x < kXcds; ++x) out.push_back(k < q[x].size() ? std::get<2>(q[x][k]) : pad);
+    for (int x = 0; x < kXcds; ++x)
+      out.push_back(k < q[x].size() ? pieces[seq_piece[q[x][k] & 0xFFFFFFFFu]].second : pad);
 }
 
 }  // namespace
@@ -302,7 +320,13 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     p->new_offsets.push_back(static_cast<int32_t>(q_row));
     p->max_len = std::max<int32_t>(p->max_len, static_cast<int32_t>(L));
     // unmasked pairs of this user's new queries
-    for (int64_t i = c; i < L; ++i) p->pairs += (i < L - T) ? (i + 1) : (L - T + 1);
+    // (a history query i sees i + 1 keys, a candidate the L - T history keys and itself)
+    {
+      const int64_t h = L - T, a = c, b = std::min(L, h);
+      if (b > a) p->pairs += (b * (b + 1) - a * (a + 1)) / 2;
+      const int64_t nc = L - std::max(c, h);
+      if (nc > 0) p->pairs += nc * (h + 1);
+    }
   }
   p->n_new = static_cast<int32_t>(q_row);
 
@@ -322,9 +346,15 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     const QBlock& qb = p->qblocks[b];
     const UserInfo& ui = p->users[qb.user];
     int64_t qa = qb.pos0, qe = qb.pos0 + qb.count;
-    int32_t ntiles = static_cast<int32_t>((qe + kTileK - 1) / kTileK);
-    for (int32_t t = 0; t < ntiles; ++t)
-      if (tile_visible(static_cast<int64_t>(t) * kTileK, qa, qe, ui.hist)) vis[b].push_back(t);
+    // tile_visible as two ranges: the band of tiles holding the block's own
+    // positions, [qa / 64, ntiles), and the tiles below min(hist, qe - 1)
+    const int32_t ntiles = static_cast<int32_t>((qe + kTileK - 1) / kTileK);
+    const int64_t lim = std::min<int64_t>(ui.hist, qe - 1);
+    const int32_t lo_end = lim > 0 ? static_cast<int32_t>(std::min<int64_t>((lim + kTileK - 1) / kTileK, ntiles)) : 0;
+    const int32_t band = static_cast<int32_t>(qa / kTileK);
+    vis[b].reserve(ntiles);
+    for (int32_t t = 0; t < lo_end; ++t) vis[b].push_back(t);
+    for (int32_t t = std::max(band, lo_end); t < ntiles; ++t) vis[b].push_back(t);
     total += static_cast<int64_t>(vis[b].size()) * H;
   }
   int64_t piece_tiles = std::min<int64_t>(
@@ -381,19 +411,24 @@ hstu_status hstu_plan_create(const hstu_batch_desc* d, hstu_plan** out) {
     }
   }
   p->n_slots = slot;
-  dispatch_order(pieces, B, H, p->items);
+  {
+    std::vector<int32_t> sel(pieces.size());
+    std::iota(sel.begin(), sel.end(), 0);
+    dispatch_order(pieces, sel, B, H, p->items);
+  }
   // The same pieces again as two consecutive orders, those of users with a
   // cached prefix first (few queries against a long prefix: the bandwidth
   // regime) and then the others (the full-recompute regime), when a request
-  // has both: instrumented runs launch them as two grids to time each.
-  {
-    std::vector<std::pair<int32_t, WorkItem>> cached_pieces, prefill_pieces;
-    for (const auto& pc : pieces)
-      (p->users[pc.second.user].start > 0 ? cached_pieces : prefill_pieces).push_back(pc);
-    if (!cached_pieces.empty() && !prefill_pieces.empty()) {
-      dispatch_order(cached_pieces, B, H, p->items_split);
+  // has both and the plan is made while split timing is on: instrumented
+  // runs launch them as two grids to time each.
+  if (timing_mode() == 2) {
+    std::vector<int32_t> cached_sel, prefill_sel;
+    for (int32_t i = 0; i < static_cast<int32_t>(pieces.size()); ++i)
+      (p->users[pieces[i].second.user].start > 0 ? cached_sel : prefill_sel).push_back(i);
+    if (!cached_sel.empty() && !prefill_sel.empty()) {
+      dispatch_order(pieces, cached_sel, B, H, p->items_split);
       p->n_split_cached = static_cast<int32_t>(p->items_split.size());
-      dispatch_order(prefill_pieces, B, H, p->items_split);
+      dispatch_order(pieces, prefill_sel, B, H, p->items_split);
     }
   }
 

@@ -511,8 +511,9 @@ class Batcher:
 
 
 def hstu_timing_enable(enable, split_attention: bool = False):
-    """enable: time every launch; split_attention: also run an attention over
-    users with and without a cached prefix as two grids, timed apart."""
+    """enable: time every launch; split_attention: also run the attention of
+    requests planned from now on over users with and without a cached prefix
+    as two grids, timed apart."""
     mode = (2 if split_attention else 1) if enable else 0
     _check(lib().hstu_timing_enable(mode), "hstu_timing_enable")
 

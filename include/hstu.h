@@ -511,8 +511,9 @@ hstu_status hstu_batcher_pending(const hstu_batcher *batcher, int32_t *n);
  * names: "layer_norm", "f1_gemm", "append", "attention", "reduce_gate",
  * "f2_gemm", "gather", "head", "bwd_attention", "bwd_gemm" (the backward's
  * products), "bwd_rows" (its row and elementwise kernels).  With enable == 2
- * the attention of a request that mixes users with a cached prefix and users
- * without one runs as two grids, recorded as "attention_cached" (the users
+ * the attention of a request planned while enable == 2 (hstu_plan_create)
+ * that mixes users with a cached prefix and users without one runs as two
+ * grids, recorded as "attention_cached" (the users
  * with a prefix: few queries against many cached keys) and
  * "attention_prefill" (the rest); other requests record "attention".  The
  * results are the same either way.  Enabling or disabling clears the

@@ -188,6 +188,96 @@ def test_plan_items_cover_visible_tiles_within_page_limit(case):
             assert got == want, (qb, hd)
 
 
+def test_plan_random_requests_pairs_and_tiles():
+    """Seeded random requests (empty users, no history, all-candidate users,
+    ragged lengths, every page size): the pair count and each (q-block,
+    head)'s covered tiles equal the enumeration of the mask."""
+    for seed in range(40):
+        rng = np.random.default_rng([seed, 0x91A])
+        B = int(rng.integers(1, 7))
+        new_len = rng.integers(0, 400, B)
+        cached_len = np.where(rng.random(B) < 0.5, rng.integers(0, 900, B), 0)
+        n_targets = np.minimum(rng.choice([0, 1, 17, 64, 400], B), new_len)
+        P = int(rng.choice([0, 16, 32, 64]))
+        L = new_len + cached_len
+        max_pages = int(max(-(-int(l) // P) for l in L)) + 1 if P else 0
+        H = int(rng.integers(1, 4))
+        p = hstu.hstu_plan_create(H, 128, new_len.astype(np.int32), cached_len.astype(np.int32),
+                                  n_targets.astype(np.int32), None, P, max_pages)
+        info = hstu.hstu_plan_get_info(p)
+        items = hstu.hstu_plan_get_items(p)
+        hstu.hstu_plan_destroy(p)
+        assert info.pairs == _visible_pairs(new_len, cached_len, n_targets), seed
+        real = items[items[:, 5] >= 0]
+        for qb, (u, pos0, count) in enumerate(_qblocks(new_len, cached_len)):
+            want = _visible_tiles(pos0, count, int(L[u]), int(n_targets[u]))
+            for hd in range(H):
+                mine = real[(real[:, 2] == qb) & (real[:, 1] == hd)]
+                got = sorted(t for (_, _, _, tb, te, _) in mine for t in want if tb <= t < te)
+                assert got == want, (seed, qb, hd)
+
+
+def _dispatch_model(pieces, H, xcds=8):
+    """The attention launch order, written out plainly: pieces (visible tiles,
+    record) of one (user, head) form a group; groups go largest first, each
+    onto the least-loaded XCD, a piece spilling to the least-loaded XCD when
+    it would lift its group's XCD above an equal share; each XCD runs its
+    pieces longest first (ties in assignment order); XCD x's k-th piece is
+    launch record 8k + x, short queues padded with slot -1."""
+    groups, order = {}, []
+    for t, rec in pieces:
+        key = (rec[0], rec[1])
+        if key not in groups:
+            groups[key] = []
+            order.append(key)
+        groups[key].append((t, rec))
+    total = sum(t for t, _ in pieces)
+    share = -(-total // xcds)
+    cost = {k: sum(t for t, _ in groups[k]) for k in order}
+    gorder = sorted(range(len(order)), key=lambda i: (-cost[order[i]], i))
+    q, load, seq = [[] for _ in range(xcds)], [0] * xcds, 0
+    for gi in gorder:
+        grp = sorted(enumerate(groups[order[gi]]), key=lambda e: (-e[1][0], e[0]))
+        home = load.index(min(load))
+        for _, (t, rec) in grp:
+            x = home if load[home] + t <= share else load.index(min(load))
+            q[x].append((t, seq, rec))
+            seq += 1
+            load[x] += t
+    for qq in q:
+        qq.sort(key=lambda e: (-e[0], e[1]))
+    depth = max((len(qq) for qq in q), default=0)
+    pad = [0, 0, 0, 0, 0, -1]
+    return [list(q[x][k][2]) if k < len(q[x]) else pad for k in range(depth) for x in range(xcds)]
+
+
+def test_plan_launch_order_matches_the_dispatch_model():
+    """The plan's launch order equals the dispatch policy written out in
+    Python, on seeded random requests (pieces recovered from the records in
+    slot order, i.e. creation order)."""
+    for seed in range(30):
+        rng = np.random.default_rng([seed, 0xD15])
+        B = int(rng.integers(1, 10))
+        new_len = rng.integers(1, 2500, B)
+        cached_len = np.where(rng.random(B) < 0.5, rng.integers(0, 5000, B), 0)
+        n_targets = np.minimum(rng.choice([0, 64, 256], B), new_len)
+        H = int(rng.integers(1, 5))
+        L = new_len + cached_len
+        p = hstu.hstu_plan_create(H, 128, new_len.astype(np.int32), cached_len.astype(np.int32),
+                                  n_targets.astype(np.int32), None, 32, int(max(-(-int(l) // 32) for l in L)))
+        items = hstu.hstu_plan_get_items(p)
+        hstu.hstu_plan_destroy(p)
+        qbs = _qblocks(new_len, cached_len)
+        real = items[items[:, 5] >= 0]
+        real = real[np.argsort(real[:, 5])]
+        pieces = []
+        for rec in real.tolist():
+            u, pos0, count = qbs[rec[2]]
+            want = _visible_tiles(pos0, count, int(L[u]), int(n_targets[u]))
+            pieces.append((sum(1 for t in want if rec[3] <= t < rec[4]), rec))
+        assert items.tolist() == _dispatch_model(pieces, H), seed
+
+
 def test_attn_stamps_validation():
     """The phase-record registration rejects a negative capacity, a missing or
     misaligned buffer, and clears with capacity 0 (no device access)."""

@@ -308,7 +308,10 @@ def test_attention_split_timing_launch_is_identical():
     H, dh, dtype = 2, 128, HSTU_BF16
     q, k, v, rab, L, users, cache, max_pages = _paged_setup(rng, dtype, H, dh, 32, new_len, cached_len,
                                                             n_targets, 4)
+    # the two orders are part of plans made while split timing is on
+    hstu.hstu_timing_enable(True, split_attention=True)
     req = runtime.prepare_attn(cache, users, new_len, n_targets, None, max_pages, H, dh)
+    hstu.hstu_timing_enable(False)
     qd = torch.from_numpy(q).to("cuda", torch.bfloat16)
     rabd = torch.from_numpy(rab).cuda()
     o1 = runtime.attention(req, qd, H * dh, rabd, dtype, cache=cache)
